@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Throughput of the hybrid sliding-window / INT8 / block-sparse attention path on one MI355X.
+
+One step is one pass over every operation of the path, each at its workload size:
+
+  ring    swa_decode_ring   batch 32, context 32768, 32 q / 8 kv heads, head_dim 128,
+                            window 128; 60 distinct ring sets per step (one per
+                            sliding-window layer of a 70-layer hybrid stack)
+  swa     swa_prefill       L 131072, 64 q / 8 kv heads, head_dim 128, window 1024
+  full    swa_prefill       same shape, full causal
+  quant   kv_quant_int8_b32 K and V of batch 16, 63488 warm tokens, 8 kv heads
+  int8    attn_decode_int8kv batch 16, context 65536 (2048 hot bf16 tokens), 32/8 heads
+  sparse  blocksparse_select_attend  L 131072, 32/8 heads, 64-token blocks, top-64, window 1024
+
+The JSON line's headline is the ring-decode workload (KV bytes per second of the
+60 ring-decode launches in each step, timed with HIP events on the stream they
+run on); every other operation is reported under "rows" with its own roofline.
+Inputs are seeded synthetic tensors (N(0,1), 1% x8 outliers for the INT8 cache)
+drawn on the GPU and resident in HBM before timing starts.  The CPU oracle is
+timed on a bounded sample of the ring-decode workload ("cpu_baseline").
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn TFLOP/s and decode KV GB/s, % of MI355X peak; oracle-exact"
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12   # dense bf16 MFMA, 2516.6 TFLOP/s
+PEAK_HBM_GBS = 8000.0                           # HBM3E, 8 TB/s
+
+# workload shapes
+RING = dict(B=32, Hq=32, Hkv=8, D=128, W=128, ctx=32768, layers=60)
+PREFILL = dict(L=131072, Hq=64, Hkv=8, D=128, W=1024)
+INT8 = dict(B=16, Hq=32, Hkv=8, D=128, ctx=65536, hot=2048)
+SPARSE = dict(L=131072, Hq=32, Hkv=8, D=128, block=64, topk=64, W=1024)
+
+
+def pairs_prefill(L: int, W: int) -> int:
+    if W <= 0 or W >= L:
+        return L * (L + 1) // 2
+    return W * (W + 1) // 2 + (L - W) * W
+
+
+def ring_bytes_per_call(c=RING) -> int:
+    """Ring K+V read, q read, out write, new-token K/V write (bf16)."""
+    ring = 2 * c["B"] * c["Hkv"] * c["W"] * c["D"] * 2
+    q = c["B"] * c["Hq"] * c["D"] * 2
+    return ring + 2 * q + 2 * c["B"] * c["Hkv"] * c["D"] * 2
+
+
+def int8_decode_bytes(c=INT8) -> int:
+    t8 = c["ctx"] - c["hot"]
+    codes = 2 * c["B"] * c["Hkv"] * t8 * c["D"]
+    scales = 2 * c["B"] * c["Hkv"] * (t8 // 32) * 4
+    hot = 2 * c["B"] * c["Hkv"] * c["hot"] * c["D"] * 2
+    q = c["B"] * c["Hq"] * c["D"] * 2
+    return codes + scales + hot + 2 * q
+
+
+def int8_quant_bytes(c=INT8) -> int:
+    n = 2 * c["B"] * c["Hkv"] * (c["ctx"] - c["hot"]) * c["D"]
+    return n * 2 + n + (n // (32 * c["D"])) * 4
+
+
+def sparse_pairs(sel, L: int, block: int, W: int) -> int:
+    """Exact visible (query, key) pairs of the block-sparse pattern, from the selection."""
+    import numpy as np
+
+    Hq, nb, topk = sel.shape
+    rows = np.arange(L, dtype=np.int64).reshape(nb, block)            # [qb, r]
+    win = np.minimum(rows + 1, W).sum(axis=1)                        # window keys per block
+    total = int(win.sum()) * Hq
+    start = rows - W + 1                                             # first window key per row
+    for h in range(Hq):
+        s = sel[h].astype(np.int64)                                  # [qb, topk]
+        valid = s >= 0
+        # keys of a selected block that lie before the row's window start
+        extra = np.clip(start[:, None, :] - (block * s)[:, :, None], 0, block)   # [qb, topk, r]
+        total += int((extra * valid[:, :, None]).sum())
+    return total
+
+
+class Timer:
+    """HIP events around work enqueued on torch's current stream (the library's stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.ms = {}
+
+    def run(self, name, fn):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.ms.setdefault(name, []).append((a, b))
+
+    def mean_ms(self, name, skip=0):
+        ev = self.ms[name][skip:]
+        return sum(a.elapsed_time(b) for a, b in ev) / max(1, len(ev))
+
+
+def cpu_baseline(target_s: float):
+    """The oracle on a bounded sample of the ring-decode workload (one thread)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from hybrid_swa_kv_amd import synth
+
+    c = RING
+    B, Hq, Hkv, D, W = c["B"], c["Hq"], c["Hkv"], c["D"], c["W"]
+    pos = np.full(B, c["ctx"] - 1, dtype=np.int64)
+    kseq = synth.bf16_bits_to_f32(synth.head_major(2, synth.K, B, Hkv, W + 1, D)).astype(np.float64)
+    vseq = synth.bf16_bits_to_f32(synth.head_major(2, synth.V, B, Hkv, W + 1, D)).astype(np.float64)
+    q = synth.bf16_bits_to_f32(synth.normal(2, synth.Q, (B, Hq, D), 1)).astype(np.float64)
+    start = pos - W
+    ring_k = oracle.ring_fill(kseq, start, pos - 1, W, np.zeros((B, Hkv, W, D)))
+    ring_v = oracle.ring_fill(vseq, start, pos - 1, W, np.zeros((B, Hkv, W, D)))
+    layers = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while layers < c["layers"]:
+            oracle.ring_append(ring_k, pos, kseq[:, :, W])
+            oracle.ring_append(ring_v, pos, vseq[:, :, W])
+            oracle.swa_decode(q, kseq, vseq, start, pos, W)
+            layers += 1
+            if time.perf_counter() - t0 >= target_s:
+                break
+    el = time.perf_counter() - t0
+    return {
+        "value": round(layers * ring_bytes_per_call() / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{layers} of the {c['layers']} ring-decode layers of one step (append + window attention, "
+                  f"batch {B}, {Hq}/{Hkv} heads, window {W}), numpy fp64, one BLAS thread, {el:.1f} s",
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--rows", default="ring,swa,full,quant,int8,sparse")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); the path has no "
+              "multi-GPU component in this build", file=sys.stderr)
+        return 2
+    rows = [r for r in args.rows.split(",") if r]
+
+    import numpy as np
+    import torch
+
+    import hybrid_swa_kv_amd as hsk
+    from hybrid_swa_kv_amd import _lib, synth
+
+    _lib.load()  # fails loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] device {torch.cuda.get_device_name(0)}; rows {rows}", file=sys.stderr, flush=True)
+
+    work = {}
+    # ---------------------------------------------------------------- setup --
+    if "ring" in rows:
+        c = RING
+        sets = []
+        for layer in range(c["layers"]):
+            rk = synth.normal_gpu(2, 100 + 2 * layer, (c["B"], c["Hkv"], c["W"], c["D"]))
+            rv = synth.normal_gpu(2, 101 + 2 * layer, (c["B"], c["Hkv"], c["W"], c["D"]))
+            q = synth.normal_gpu(2, 1000 + layer, (c["B"], c["Hq"], c["D"]))
+            kn = synth.normal_gpu(2, 2000 + layer, (c["B"], c["Hkv"], c["D"]))
+            vn = synth.normal_gpu(2, 3000 + layer, (c["B"], c["Hkv"], c["D"]))
+            sets.append((q, kn, vn, rk, rv, torch.empty_like(q)))
+        pos = torch.full((c["B"],), c["ctx"] - 1, dtype=torch.int32, device=dev)
+        slots = torch.empty(c["B"], dtype=torch.int32, device=dev)
+
+        def ring_step(sets=sets, pos=pos, slots=slots):
+            for (q, kn, vn, rk, rv, out) in sets:
+                hsk.swa_decode_ring(q, kn, vn, rk, rv, pos, out=out, slot_out=slots)
+
+        work["ring"] = ring_step
+    if "swa" in rows or "full" in rows:
+        c = PREFILL
+        pq = synth.normal_gpu(3, synth.Q, (c["L"], c["Hq"], c["D"]))
+        pk = synth.normal_gpu(3, synth.K, (c["L"], c["Hkv"], c["D"]))
+        pv = synth.normal_gpu(3, synth.V, (c["L"], c["Hkv"], c["D"]))
+        pout = torch.empty_like(pq)
+        if "swa" in rows:
+            work["swa"] = lambda: hsk.swa_prefill(pq, pk, pv, PREFILL["W"], out=pout)
+        if "full" in rows:
+            work["full"] = lambda: hsk.swa_prefill(pq, pk, pv, 0, out=pout)
+    if "quant" in rows or "int8" in rows:
+        c = INT8
+        t8 = c["ctx"] - c["hot"]
+        kx = synth.normal_gpu(4, synth.K, (c["B"], c["Hkv"], c["ctx"], c["D"]), outlier_p=0.01)
+        vx = synth.normal_gpu(4, synth.V, (c["B"], c["Hkv"], c["ctx"], c["D"]), outlier_p=0.01)
+        kwarm, vwarm = kx[:, :, :t8].contiguous(), vx[:, :, :t8].contiguous()
+        khot, vhot = kx[:, :, t8:].contiguous(), vx[:, :, t8:].contiguous()
+        del kx, vx
+        iq = synth.normal_gpu(4, synth.Q, (c["B"], c["Hq"], c["D"]))
+        kc = torch.empty(kwarm.shape, dtype=torch.int8, device=dev)
+        vc = torch.empty_like(kc)
+        ks = torch.empty((c["B"], c["Hkv"], t8 // 32), dtype=torch.float32, device=dev)
+        vs = torch.empty_like(ks)
+        hsk.kv_quant_int8_b32(kwarm, kc, ks)
+        hsk.kv_quant_int8_b32(vwarm, vc, vs)
+        iout = torch.empty_like(iq)
+        iws = torch.empty(hsk.attn_decode_int8kv_workspace_size(c["B"], c["Hq"], c["Hkv"], c["D"], t8, c["hot"]),
+                          dtype=torch.uint8, device=dev)
+        if "quant" in rows:
+            def quant_step():
+                hsk.kv_quant_int8_b32(kwarm, kc, ks)
+                hsk.kv_quant_int8_b32(vwarm, vc, vs)
+            work["quant"] = quant_step
+        if "int8" in rows:
+            work["int8"] = lambda: hsk.attn_decode_int8kv(iq, kc, ks, vc, vs, khot, vhot, out=iout, workspace=iws)
+    if "sparse" in rows:
+        c = SPARSE
+        sq = synth.normal_gpu(5, synth.Q, (c["L"], c["Hq"], c["D"]))
+        sk = synth.normal_gpu(5, synth.K, (c["L"], c["Hkv"], c["D"]))
+        sv = synth.normal_gpu(5, synth.V, (c["L"], c["Hkv"], c["D"]))
+        sout = torch.empty_like(sq)
+        ssel = torch.empty((c["Hq"], c["L"] // c["block"], c["topk"]), dtype=torch.int32, device=dev)
+        sws = torch.empty(hsk.blocksparse_workspace_size(c["L"], c["Hq"], c["Hkv"], c["D"], c["block"], c["topk"]),
+                          dtype=torch.uint8, device=dev)
+        work["sparse"] = lambda: hsk.blocksparse_select_attend(sq, sk, sv, c["block"], c["topk"], c["W"],
+                                                               out=sout, sel=ssel, workspace=sws)
+    torch.cuda.synchronize()
+    print("[bench] inputs resident; warming up", file=sys.stderr, flush=True)
+
+    # ----------------------------------------------------------------- timing --
+    timer = Timer(torch)
+
+    def step():
+        for name in rows:
+            timer.run(name, work[name])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] timing", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+        print(f"[bench] step {i + 1}/{args.steps} enqueued", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    res = {}
+    if "ring" in rows:
+        ms = timer.mean_ms("ring", args.warmup)
+        per_launch_us = ms * 1e3 / RING["layers"]
+        gbs = ring_bytes_per_call() / (per_launch_us * 1e-6) / 1e9
+        res["ring"] = {"ms_per_step": round(ms, 4), "us_per_launch": round(per_launch_us, 3),
+                       "bytes_per_launch": ring_bytes_per_call(), "GB/s": round(gbs, 1),
+                       "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    for name, W in (("swa", PREFILL["W"]), ("full", 0)):
+        if name in rows:
+            c = PREFILL
+            ms = timer.mean_ms(name, args.warmup)
+            flops = 4 * c["D"] * c["Hq"] * pairs_prefill(c["L"], W)
+            tf = flops / (ms * 1e-3) / 1e12
+            res[name] = {"ms": round(ms, 3), "flop": flops, "TFLOP/s": round(tf, 1),
+                         "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    if "swa" in rows and "full" in rows:
+        res["full_over_swa_flop_ratio"] = round(res["full"]["flop"] / res["swa"]["flop"], 4)
+    if "quant" in rows:
+        ms = timer.mean_ms("quant", args.warmup)
+        gbs = int8_quant_bytes() / (ms * 1e-3) / 1e9
+        res["quant"] = {"ms": round(ms, 4), "bytes": int8_quant_bytes(), "GB/s": round(gbs, 1),
+                        "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    if "int8" in rows:
+        ms = timer.mean_ms("int8", args.warmup)
+        gbs = int8_decode_bytes() / (ms * 1e-3) / 1e9
+        res["int8"] = {"ms": round(ms, 4), "bytes": int8_decode_bytes(), "GB/s": round(gbs, 1),
+                       "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    if "sparse" in rows:
+        c = SPARSE
+        ms = timer.mean_ms("sparse", args.warmup)
+        pairs = sparse_pairs(ssel.cpu().numpy(), c["L"], c["block"], c["W"])
+        flops = 4 * c["D"] * pairs
+        tf = flops / (ms * 1e-3) / 1e12
+        res["sparse"] = {"ms": round(ms, 3), "visible_pairs": pairs, "flop": flops, "TFLOP/s": round(tf, 1),
+                         "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+    line = {
+        "metric": METRIC,
+        "value": res["ring"]["GB/s"] if "ring" in res else None,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "swa_ring_decode", "batch": RING["B"], "context": RING["ctx"],
+                   "q_heads": RING["Hq"], "kv_heads": RING["Hkv"], "head_dim": RING["D"],
+                   "window": RING["W"], "ring_sets_per_step": RING["layers"],
+                   "value_basis": "KV bytes of the ring-decode launches / their HIP-event time; "
+                                  "ms_per_step covers every row"},
+    }
+    if "ring" in res:
+        line["roofline"] = {"kernel": "ring_decode_kernel", "bound": "hbm",
+                            "achieved": res["ring"]["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": res["ring"]["frac_hbm_peak"], "traffic": None}
+    line["rows"] = res
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,54 @@
+"""ctypes loader for libhybrid_swa_kv.so (argument types only, no logic)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhybrid_swa_kv.so")
+
+# every symbol declared in include/hybrid_swa_kv.h
+EXPORTS = (
+    "hsk_strerror",
+    "hsk_abi_version",
+    "swa_prefill",
+    "swa_decode_ring",
+    "kv_quant_int8_b32",
+    "attn_decode_int8kv",
+    "attn_decode_int8kv_workspace_size",
+    "blocksparse_select_attend",
+    "blocksparse_workspace_size",
+)
+
+_P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+_SIGS = {
+    "hsk_strerror": (ctypes.c_char_p, [_I]),
+    "hsk_abi_version": (_I, []),
+    "swa_prefill": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _P]),
+    "swa_decode_ring": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "kv_quant_int8_b32": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    "attn_decode_int8kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
+    "attn_decode_int8kv_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
+    "blocksparse_select_attend": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
+    "blocksparse_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the library once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m hybrid_swa_kv_amd.build` "
+                "(the HIP library is the only implementation; there is no fallback)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib

@@ -1,0 +1,205 @@
+// C ABI: host-side argument validation and kernel dispatch.
+// Nothing here allocates device memory or keeps state between calls.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "hybrid_swa_kv.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+inline bool head_dim_ok(int D) { return D == 64 || D == 128; }
+inline float log2e_times(float scale) { return (float)((double)scale * 1.4426950408889634); }
+
+inline int finish(hipError_t e) { return e == hipSuccess ? HSK_OK : HSK_ERR_HIP; }
+
+int check_heads(int Hq, int Hkv, int D) {
+  if (Hq <= 0 || Hkv <= 0 || D <= 0) return HSK_ERR_SHAPE;
+  if (Hq % Hkv != 0) return HSK_ERR_SHAPE;
+  if (!head_dim_ok(D)) return HSK_ERR_UNSUPPORTED;
+  return HSK_OK;
+}
+
+size_t int8_ws_bytes(int B, int Hq, int Hkv, int D, int T8, int Th) {
+  int split8, splith, ns8, nsh;
+  hsk::int8_decode_plan(B, Hkv, T8, Th, &split8, &splith, &ns8, &nsh);
+  return (size_t)B * Hkv * (size_t)(ns8 + nsh) * (size_t)(Hq / Hkv) * (size_t)(D + 2) * sizeof(float);
+}
+
+size_t bs_ws_bytes(int L, int Hq, int Hkv, int D, int block) {
+  const size_t nb = (size_t)L / block;
+  return ((size_t)Hq + Hkv) * nb * D * sizeof(double);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hsk_strerror(int status) {
+  switch (status) {
+    case HSK_OK: return "ok";
+    case HSK_ERR_NULL: return "a required pointer is NULL";
+    case HSK_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case HSK_ERR_UNSUPPORTED: return "unsupported configuration (head_dim, group size, dtype or block)";
+    case HSK_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case HSK_ERR_WORKSPACE: return "workspace missing or too small";
+    case HSK_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int hsk_abi_version(void) { return kAbiVersion; }
+
+int swa_prefill(const void* q, const void* k, const void* v, void* out, int B, int L, int Hq, int Hkv,
+                int D, int window, float scale, int dtype, void* ring_k, void* ring_v, int ring_w,
+                void* stream) {
+  if (!q || !k || !v || !out) return HSK_ERR_NULL;
+  if ((ring_k == nullptr) != (ring_v == nullptr)) return HSK_ERR_NULL;
+  if (B <= 0 || L <= 0) return HSK_ERR_SHAPE;
+  if (int rc = check_heads(Hq, Hkv, D)) return rc;
+  if (dtype != HSK_F32 && dtype != HSK_BF16) return HSK_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return HSK_ERR_SHAPE;
+  if ((long long)L > (1ll << 30) || (long long)B * L * Hq > (1ll << 31) - 1) return HSK_ERR_SHAPE;
+  if (ring_k && ring_w <= 0) return HSK_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return HSK_ERR_ALIGN;
+  if (ring_k && (!aligned16(ring_k) || !aligned16(ring_v))) return HSK_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  hsk::PrefillArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)out;
+  a.B = B; a.L = L; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
+  a.window = (window <= 0 || window >= L) ? L + 256 : window;
+  a.scale = scale;
+  a.scale_log2 = log2e_times(scale);
+  hipError_t e = dtype == HSK_BF16 ? hsk::launch_prefill_bf16(a, s) : hsk::launch_prefill_f32(a, s);
+  if (e != hipSuccess) return HSK_ERR_HIP;
+  if (ring_k) {
+    hsk::RingCopyArgs r{};
+    r.k = k; r.v = v; r.ring_k = ring_k; r.ring_v = ring_v;
+    r.B = B; r.L = L; r.Hkv = Hkv; r.W = ring_w;
+    r.row_bytes = D * (dtype == HSK_BF16 ? 2 : 4);
+    e = hsk::launch_prefill_ring(r, s);
+  }
+  return finish(e);
+}
+
+int swa_decode_ring(const void* q, const void* k_new, const void* v_new, void* ring_k, void* ring_v,
+                    const int32_t* pos, void* out, int32_t* slot_out, int B, int Hq, int Hkv, int D,
+                    int W, float scale, void* stream) {
+  if (!q || !k_new || !v_new || !ring_k || !ring_v || !pos || !out) return HSK_ERR_NULL;
+  if (B <= 0 || W <= 0 || W > 65536) return HSK_ERR_SHAPE;
+  if (int rc = check_heads(Hq, Hkv, D)) return rc;
+  if (!std::isfinite(scale)) return HSK_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(ring_k) ||
+      !aligned16(ring_v) || !aligned16(out) || !aligned4(pos) || (slot_out && !aligned4(slot_out)))
+    return HSK_ERR_ALIGN;
+  hsk::RingDecodeArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k_new = (const uint16_t*)k_new;
+  a.v_new = (const uint16_t*)v_new;
+  a.ring_k = (uint16_t*)ring_k;
+  a.ring_v = (uint16_t*)ring_v;
+  a.pos = pos;
+  a.out = (uint16_t*)out;
+  a.slot_out = slot_out;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.W = W;
+  a.scale_log2 = log2e_times(scale);
+  return finish(hsk::launch_ring_decode(a, (hipStream_t)stream));
+}
+
+int kv_quant_int8_b32(const void* x, int8_t* codes, float* scales, int B, int Hkv, int T, int D,
+                      void* stream) {
+  if (!x || !codes || !scales) return HSK_ERR_NULL;
+  if (B <= 0 || Hkv <= 0 || T < 0 || T % 32 != 0) return HSK_ERR_SHAPE;
+  if (!head_dim_ok(D)) return HSK_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(codes) || !aligned4(scales)) return HSK_ERR_ALIGN;
+  if (T == 0) return HSK_OK;
+  hsk::QuantArgs a{};
+  a.x = (const uint16_t*)x;
+  a.codes = codes;
+  a.scales = scales;
+  a.nblocks = (long)B * Hkv * (T / 32);
+  a.D = D;
+  return finish(hsk::launch_quant_b32(a, (hipStream_t)stream));
+}
+
+size_t attn_decode_int8kv_workspace_size(int B, int Hq, int Hkv, int D, int T8, int Th) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || T8 < 0 || Th <= 0) return 0;
+  return int8_ws_bytes(B, Hq, Hkv, D, T8, Th);
+}
+
+int attn_decode_int8kv(const void* q, const int8_t* k_codes, const float* k_scales, const int8_t* v_codes,
+                       const float* v_scales, const void* k_hot, const void* v_hot, void* out, int B, int Hq,
+                       int Hkv, int D, int T8, int Th, float scale, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!q || !k_hot || !v_hot || !out) return HSK_ERR_NULL;
+  if (T8 > 0 && (!k_codes || !k_scales || !v_codes || !v_scales)) return HSK_ERR_NULL;
+  if (B <= 0 || T8 < 0 || T8 % 32 != 0 || Th <= 0) return HSK_ERR_SHAPE;
+  if (int rc = check_heads(Hq, Hkv, D)) return rc;
+  if (Hq / Hkv > 16) return HSK_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return HSK_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_hot) || !aligned16(v_hot) || !aligned16(out)) return HSK_ERR_ALIGN;
+  if (T8 > 0 && (!aligned16(k_codes) || !aligned16(v_codes) || !aligned4(k_scales) || !aligned4(v_scales)))
+    return HSK_ERR_ALIGN;
+  const size_t need = int8_ws_bytes(B, Hq, Hkv, D, T8, Th);
+  if (!workspace || workspace_bytes < need) return HSK_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return HSK_ERR_ALIGN;
+  hsk::Int8DecodeArgs a{};
+  a.q = (const uint16_t*)q;
+  a.kc = k_codes; a.ks = k_scales; a.vc = v_codes; a.vs = v_scales;
+  a.kh = (const uint16_t*)k_hot;
+  a.vh = (const uint16_t*)v_hot;
+  a.out = (uint16_t*)out;
+  a.ws = (float*)workspace;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T8 = T8; a.Th = Th;
+  a.scale_log2 = log2e_times(scale);
+  hsk::int8_decode_plan(B, Hkv, T8, Th, &a.split8, &a.splith, &a.ns8, &a.nsh);
+  return finish(hsk::launch_int8_decode(a, (hipStream_t)stream));
+}
+
+size_t blocksparse_workspace_size(int L, int Hq, int Hkv, int D, int block, int topk) {
+  (void)topk;
+  if (L <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || block <= 0) return 0;
+  return bs_ws_bytes(L, Hq, Hkv, D, block);
+}
+
+int blocksparse_select_attend(const void* q, const void* k, const void* v, void* out, int32_t* sel, int L,
+                              int Hq, int Hkv, int D, int block, int topk, int window, float scale,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !out) return HSK_ERR_NULL;
+  if (topk > 0 && !sel) return HSK_ERR_NULL;
+  if (L <= 0 || window < 1 || topk < 0) return HSK_ERR_SHAPE;
+  if (int rc = check_heads(Hq, Hkv, D)) return rc;
+  if (block != 64 || topk > 256) return HSK_ERR_UNSUPPORTED;
+  if (L % block != 0) return HSK_ERR_SHAPE;
+  if (L / block > 4096) return HSK_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return HSK_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (sel && !aligned4(sel)))
+    return HSK_ERR_ALIGN;
+  const size_t need = bs_ws_bytes(L, Hq, Hkv, D, block);
+  if (!workspace || workspace_bytes < need) return HSK_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return HSK_ERR_ALIGN;
+  hsk::BlockSparseArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.out = (uint16_t*)out;
+  a.sel = sel;
+  a.L = L; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.block = block; a.topk = topk;
+  a.window = window >= L ? L + 256 : window;
+  a.nb = L / block;
+  a.qsum = (double*)workspace;
+  a.ksum = a.qsum + (size_t)Hq * a.nb * D;
+  a.scale_log2 = log2e_times(scale);
+  return finish(hsk::launch_blocksparse(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

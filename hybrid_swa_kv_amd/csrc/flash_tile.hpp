@@ -1,0 +1,199 @@
+// The attention tile pipeline shared by the sliding-window / full prefill and the
+// block-sparse union attention (gfx950, bf16 in, fp32 accumulate).
+//
+// A wave owns 32 query rows of one head.  For each 64-key tile staged in LDS it
+//   1. computes S^T = K * Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS,
+//      B = the wave's Q fragment held in registers for the whole loop), so lane l
+//      holds 32 scores of query row l%32 and lane l^32 the other 32;
+//   2. masks edge tiles, runs the online softmax in the log2 domain (row max via
+//      one permlane32 swap, v_exp_f32), rescales the accumulator;
+//   3. accumulates O^T += V^T * P^T: P^T is the softmax output in place (its key
+//      order is matched by the V^T operand), V^T comes from LDS through two
+//      ds_read_b64_tr_b16 per MFMA.
+// K/V tiles are stored in LDS with a 16-byte-chunk XOR swizzle.
+#pragma once
+
+#include "common.hpp"
+
+namespace hsk {
+
+constexpr int FT_BN = 64;  // keys per tile
+
+template <int D>
+struct FtCfg {
+  static constexpr int NCH = D / 8;          // 16-byte chunks per K/V row
+  static constexpr int TILE = FT_BN * D * 2;  // bytes of one K (or V) tile
+  static constexpr int DC = D / 16;          // k-steps of S^T
+  static constexpr int DB = D / 32;          // 32-row d blocks of O^T
+};
+
+template <int NCH>
+__device__ __forceinline__ int ft_swz(int row) { return (2 * (row & 7)) & (NCH - 1); }
+
+template <int NCH>
+__device__ __forceinline__ int ft_off(int row, int chunk) {
+  return row * NCH * 16 + ((chunk ^ ft_swz<NCH>(row)) << 4);
+}
+
+// Global -> registers -> LDS staging of one K and one V tile by NT threads.
+template <int D, int NT>
+struct TileStage {
+  using C = FtCfg<D>;
+  static constexpr int CPT = FT_BN * C::NCH / NT;
+  uint4 kreg[CPT], vreg[CPT];
+
+  // rows kt*64 .. kt*64+63 of kbase/vbase (row stride in elements); rows >= nrows read as 0
+  __device__ __forceinline__ void load(const uint16_t* kbase, const uint16_t* vbase, size_t stride,
+                                       int kt, int nrows) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int u = i * NT + (int)threadIdx.x;
+      const int r = u / C::NCH, c = u % C::NCH;
+      const int kp = kt * FT_BN + r;
+      if (kp < nrows) {
+        kreg[i] = *(const uint4*)(kbase + (size_t)kp * stride + c * 8);
+        vreg[i] = *(const uint4*)(vbase + (size_t)kp * stride + c * 8);
+      } else {
+        kreg[i] = make_uint4(0, 0, 0, 0);
+        vreg[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(char* kv_lds) const {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int u = i * NT + (int)threadIdx.x;
+      const int r = u / C::NCH, c = u % C::NCH;
+      const int off = ft_off<C::NCH>(r, c);
+      *(uint4*)(kv_lds + off) = kreg[i];
+      *(uint4*)(kv_lds + C::TILE + off) = vreg[i];
+    }
+  }
+};
+
+template <int D>
+struct FlashWave {
+  using C = FtCfg<D>;
+  bf16x8 qf[C::DC];
+  f32x16 o[C::DB];
+  float m, l;
+
+  // qrow: this lane's query row (D values) or nullptr for rows past the end
+  __device__ __forceinline__ void init(const uint16_t* qrow) {
+    const int lane = __lane_id();
+#pragma unroll
+    for (int c = 0; c < C::DC; ++c) {
+      uint4 t = make_uint4(0, 0, 0, 0);
+      if (qrow) t = *(const uint4*)(qrow + 16 * c + 8 * (lane >> 5));
+      qf[c] = as_bf16x8(t);
+    }
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+    m = kNegInf;
+    l = 0.f;
+  }
+
+  // One 64-key tile at key position k0 held in LDS (K at ks, V at vs).
+  // r0: first query row of the wave; row: this lane's row; visibility is
+  // 0 <= row - key < W unless `full` (every key of the tile visible to every row).
+  __device__ __forceinline__ void tile(const char* ks, const char* vs, int k0, int r0, int row,
+                                       int W, bool full, float scale_log2) {
+    const int lane = __lane_id();
+    bool need_mask = false;
+    if (!full) {
+      if ((k0 > r0 + 31) || (k0 + FT_BN - 1 < r0 - W + 1)) return;  // nothing visible
+      need_mask = !((k0 + FT_BN - 1 <= r0) && (r0 + 31 - k0 < W));
+    }
+    f32x16 s[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[sub][r] = 0.f;
+      const int key = 32 * sub + (lane & 31);
+#pragma unroll
+      for (int c = 0; c < C::DC; ++c) {
+        const int ch = 2 * c + (lane >> 5);
+        const bf16x8 ka = *(const bf16x8*)(ks + ft_off<C::NCH>(key, ch));
+        s[sub] = mfma32(ka, qf[c], s[sub]);
+      }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[sub][r] * scale_log2;
+        if (need_mask) {
+          const int kp = k0 + 32 * sub + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int dd = row - kp;
+          if (dd < 0 || dd >= W) x = kNegInf;
+        }
+        s[sub][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m, mx);
+    const float base = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(m - base);
+    float ps = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(s[sub][r] - base);
+        s[sub][r] = p;
+        ps += p;
+      }
+    l = l * alpha + ps;
+    m = m_new;
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+
+    const int gq = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int kap = 0; kap < 4; ++kap) {
+      const int sub = kap >> 1, half = kap & 1;
+      u32x4 pw;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pw[j] = pack_bf16x2(s[sub][8 * half + 2 * j], s[sub][8 * half + 2 * j + 1]);
+      const bf16x8 pb = as_bf16x8(pw);
+      // k-slot j of lane group gq/2 <-> key 16 kap + 4 (gq/2) + j (j < 4) or + 8 + (j - 4)
+      const int kr = 16 * kap + 4 * (gq >> 1) + (sl >> 2);
+#pragma unroll
+      for (int d = 0; d < C::DB; ++d) {
+        const int col = 32 * d + 16 * (gq & 1) + 4 * (sl & 3);
+        const int o0 = ft_off<C::NCH>(kr, col >> 3) + ((col & 7) << 1);
+        const int o1 = ft_off<C::NCH>(kr + 8, col >> 3) + ((col & 7) << 1);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + o0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + o1));
+        typedef __attribute__((ext_vector_type(8))) short s16x8;
+        const s16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[d] = mfma32(__builtin_bit_cast(bf16x8, va), pb, o[d]);
+      }
+    }
+  }
+
+  // normalise and store this lane's row (orow = nullptr: row not stored)
+  __device__ __forceinline__ void store(uint16_t* orow) {
+    const int lane = __lane_id();
+    const float lt = l + xor32(l);
+    const float inv = 1.f / lt;
+    if (!orow) return;
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = 32 * d + 8 * r4 + 4 * (lane >> 5);
+        uint2 st;
+        st.x = pack_bf16x2(o[d][4 * r4 + 0] * inv, o[d][4 * r4 + 1] * inv);
+        st.y = pack_bf16x2(o[d][4 * r4 + 2] * inv, o[d][4 * r4 + 3] * inv);
+        *(uint2*)(orow + d0) = st;
+      }
+  }
+};
+
+}  // namespace hsk

@@ -1,0 +1,89 @@
+// Host-side launch interface between the C ABI (abi.cpp) and the kernels.
+// Every launcher assumes its arguments were validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hsk {
+
+struct PrefillArgs {
+  const uint16_t* q;  // bf16 bits, or fp32 reinterpreted, [B, L, Hq, D]
+  const uint16_t* k;  // [B, L, Hkv, D]
+  const uint16_t* v;
+  uint16_t* o;
+  int B, L, Hq, Hkv, D;
+  int window;        // effective window, >= 1 (full causal passed as L + 1 or more)
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+  int nqb, total;    // filled by the launcher
+};
+
+struct RingCopyArgs {
+  const void* k;  // [B, L, Hkv, D]
+  const void* v;
+  void* ring_k;   // [B, Hkv, W, D]
+  void* ring_v;
+  int B, L, Hkv, W, row_bytes;
+};
+
+struct RingDecodeArgs {
+  const uint16_t* q;      // [B, Hq, D]
+  const uint16_t* k_new;  // [B, Hkv, D]
+  const uint16_t* v_new;
+  uint16_t* ring_k;       // [B, Hkv, W, D]
+  uint16_t* ring_v;
+  const int32_t* pos;     // [B]
+  uint16_t* out;          // [B, Hq, D]
+  int32_t* slot_out;      // [B] or null
+  int B, Hq, Hkv, D, W;
+  float scale_log2;
+};
+
+struct QuantArgs {
+  const uint16_t* x;  // [B, Hkv, T, D]
+  int8_t* codes;      // [B, Hkv, T, D]
+  float* scales;      // [B, Hkv, T/32]
+  long nblocks;       // B * Hkv * T / 32
+  int D;
+};
+
+struct Int8DecodeArgs {
+  const uint16_t* q;  // [B, Hq, D]
+  const int8_t* kc;   // [B, Hkv, T8, D]
+  const float* ks;    // [B, Hkv, T8/32]
+  const int8_t* vc;
+  const float* vs;
+  const uint16_t* kh;  // [B, Hkv, Th, D]
+  const uint16_t* vh;
+  uint16_t* out;       // [B, Hq, D]
+  float* ws;           // partials [B*Hkv][nsplit][G][D + 2]
+  int B, Hq, Hkv, D, T8, Th;
+  float scale_log2;
+  int split8, splith;  // tokens per split in the int8 / hot region
+  int ns8, nsh;        // number of splits in each region
+};
+
+struct BlockSparseArgs {
+  const uint16_t* q;  // [L, Hq, D]
+  const uint16_t* k;  // [L, Hkv, D]
+  const uint16_t* v;
+  uint16_t* out;      // [L, Hq, D]
+  int32_t* sel;       // [Hq, nb, topk]
+  double* qsum;       // [Hq, nb, D]
+  double* ksum;       // [Hkv, nb, D]
+  int L, Hq, Hkv, D, block, topk, window, nb;
+  float scale_log2;
+};
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_ring(const RingCopyArgs& a, hipStream_t s);
+hipError_t launch_ring_decode(const RingDecodeArgs& a, hipStream_t s);
+hipError_t launch_quant_b32(const QuantArgs& a, hipStream_t s);
+void int8_decode_plan(int B, int Hkv, int T8, int Th, int* split8, int* splith, int* ns8, int* nsh);
+hipError_t launch_int8_decode(const Int8DecodeArgs& a, hipStream_t s);
+hipError_t launch_blocksparse(const BlockSparseArgs& a, hipStream_t s);
+
+}  // namespace hsk

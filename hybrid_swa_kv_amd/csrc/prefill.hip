@@ -1,0 +1,170 @@
+// Causal sliding-window / full GQA prefill for gfx950.
+//
+// bf16 path: one workgroup = 4 waves = 128 query rows of one head; the key axis
+// is walked in 64-key tiles staged in LDS (double buffered).  Each wave owns 32
+// query rows and computes S^T = K * Q^T with v_mfma_f32_32x32x16_bf16, so every
+// lane holds 32 of its row's 64 scores and the other 32 sit in lane ^ 32: the
+// online softmax needs one permlane32 swap per tile.  P stays in registers and
+// feeds O^T += V^T * P^T directly; V^T comes out of LDS with ds_read_b64_tr_b16.
+// Tiles wholly outside a wave's window are skipped; only edge tiles are masked.
+//
+// fp32 path: plain per-(row, head) online softmax in fp32 for small cases.
+#include "common.hpp"
+#include "flash_tile.hpp"
+#include "kernels.hpp"
+
+namespace hsk {
+
+namespace {
+
+constexpr int PF_BM = 128;
+constexpr int PF_THREADS = 256;
+
+template <int D>
+__global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
+  using C = FtCfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * C::TILE];
+
+  // XCD-aware order: consecutive logical units share (b, kv head, query block)
+  // and land on the same XCD (workgroups are dealt round-robin over 8 XCDs).
+  const int per = gridDim.x >> 3;
+  const int n = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (n >= a.total) return;
+  const int G = a.Hq / a.Hkv;
+  const int hh = n % G;
+  const int t1 = n / G;
+  const int qi = t1 % a.nqb;
+  const int t2 = t1 / a.nqb;
+  const int g = t2 % a.Hkv;
+  const int b = t2 / a.Hkv;
+  const int qblk = a.nqb - 1 - qi;  // longest rows first
+  const int h = g * G + hh;
+  const int L = a.L;
+  const int W = a.window;           // >= 1; full causal is passed as a window > L
+  const int q0 = qblk * PF_BM;
+  const int lane = __lane_id();
+  const int w = threadIdx.x >> 6;
+  const int r0 = q0 + 32 * w;        // first row of this wave
+  const int row = r0 + (lane & 31);  // this lane's query row
+
+  const int k_lo = max(0, q0 - W + 1);
+  const int k_hi = min(L, q0 + PF_BM) - 1;
+  const int kt0 = k_lo / FT_BN;
+  const int ntiles = k_hi / FT_BN - kt0 + 1;
+
+  FlashWave<D> fw;
+  fw.init(row < L ? a.q + ((size_t)(b * (size_t)L + row) * a.Hq + h) * D : nullptr);
+
+  const size_t stride = (size_t)a.Hkv * D;
+  const uint16_t* kbase = a.k + ((size_t)b * L * a.Hkv + g) * D;
+  const uint16_t* vbase = a.v + ((size_t)b * L * a.Hkv + g) * D;
+  TileStage<D, PF_THREADS> stg;
+  stg.load(kbase, vbase, stride, kt0, L);
+  stg.store(smem);
+
+  for (int it = 0; it < ntiles; ++it) {
+    __syncthreads();
+    const int kt = kt0 + it;
+    if (it + 1 < ntiles) stg.load(kbase, vbase, stride, kt + 1, L);
+    const char* ks = smem + (it & 1) * 2 * C::TILE;
+    fw.tile(ks, ks + C::TILE, kt * FT_BN, r0, row, W, false, a.scale_log2);
+    if (it + 1 < ntiles) stg.store(smem + ((it + 1) & 1) * 2 * C::TILE);
+  }
+  fw.store(row < L ? a.o + ((size_t)(b * (size_t)L + row) * a.Hq + h) * D : nullptr);
+}
+
+// fp32: one thread per (b, row, head); exact fp32 arithmetic with expf.
+template <int D>
+__global__ __launch_bounds__(128) void prefill_f32_kernel(PrefillArgs a) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long total = (long)a.B * a.L * a.Hq;
+  if (idx >= total) return;
+  const int h = (int)(idx % a.Hq);
+  const long t = idx / a.Hq;
+  const int row = (int)(t % a.L);
+  const int b = (int)(t / a.L);
+  const int G = a.Hq / a.Hkv;
+  const int g = h / G;
+  const float* qf = (const float*)a.q + ((size_t)(b * (size_t)a.L + row) * a.Hq + h) * D;
+  const float* kf = (const float*)a.k + ((size_t)b * a.L * a.Hkv + g) * D;
+  const float* vf = (const float*)a.v + ((size_t)b * a.L * a.Hkv + g) * D;
+  const size_t rs = (size_t)a.Hkv * D;
+  float q[D], acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) { q[d] = qf[d]; acc[d] = 0.f; }
+  const int lo = max(0, row - a.window + 1);
+  float m = kNegInf, l = 0.f;
+  for (int j = lo; j <= row; ++j) {
+    const float* kr = kf + (size_t)j * rs;
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) s = fmaf(q[d], kr[d], s);
+    s *= a.scale;
+    const float m_new = fmaxf(m, s);
+    const float alpha = expf(m - m_new);
+    const float p = expf(s - m_new);
+    l = l * alpha + p;
+    const float* vr = vf + (size_t)j * rs;
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vr[d], acc[d] * alpha);
+    m = m_new;
+  }
+  float* orow = (float*)a.o + ((size_t)(b * (size_t)a.L + row) * a.Hq + h) * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) orow[d] = acc[d] / l;
+}
+
+// ring copy: positions max(0, L-W) .. L-1 -> slot p mod W of [B, Hkv, W, D]
+__global__ void prefill_ring_kernel(RingCopyArgs a) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;   // one 16-byte chunk
+  const int cpr = a.row_bytes / 16;
+  const int n = min(a.L, a.W);
+  const long total = (long)a.B * a.Hkv * n * cpr;
+  if (idx >= total) return;
+  const int c = (int)(idx % cpr);
+  long t = idx / cpr;
+  const int i = (int)(t % n);
+  t /= n;
+  const int g = (int)(t % a.Hkv);
+  const int b = (int)(t / a.Hkv);
+  const int p = a.L - n + i;
+  const int slot = p % a.W;
+  const size_t src = (((size_t)b * a.L + p) * a.Hkv + g) * a.row_bytes + (size_t)c * 16;
+  const size_t dst = (((size_t)b * a.Hkv + g) * a.W + slot) * a.row_bytes + (size_t)c * 16;
+  *(uint4*)((char*)a.ring_k + dst) = *(const uint4*)((const char*)a.k + src);
+  *(uint4*)((char*)a.ring_v + dst) = *(const uint4*)((const char*)a.v + src);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const PrefillArgs& in, hipStream_t stream) {
+  PrefillArgs a = in;
+  a.nqb = (a.L + PF_BM - 1) / PF_BM;
+  a.total = a.B * a.Hq * a.nqb;
+  const int grid = (a.total + 7) / 8 * 8;
+  if (a.D == 128)
+    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(grid), dim3(PF_THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(grid), dim3(PF_THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
+  const long total = (long)a.B * a.L * a.Hq;
+  const int grid = (int)((total + 127) / 128);
+  if (a.D == 128)
+    hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3(grid), dim3(128), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3(grid), dim3(128), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_ring(const RingCopyArgs& a, hipStream_t stream) {
+  const long total = (long)a.B * a.Hkv * (long)(a.L < a.W ? a.L : a.W) * (a.row_bytes / 16);
+  if (total == 0) return hipSuccess;
+  const int grid = (int)((total + 255) / 256);
+  hipLaunchKernelGGL(prefill_ring_kernel, dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace hsk

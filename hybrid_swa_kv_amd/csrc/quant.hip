@@ -1,0 +1,69 @@
+// INT8 block-wise KV encoder: one wave per (sequence, KV head, 32-token block).
+//
+// The block's 32 x D bf16 values are read with coalesced 16-byte loads (D/2
+// values per lane), the absolute maximum is reduced across the wave, and every
+// value is divided by the block scale with the IEEE (correctly rounded) fp32
+// division, rounded half-to-even (v_rndne_f32) and clamped to [-127, 127].
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace hsk {
+
+namespace {
+
+constexpr int QZ_THREADS = 256;
+
+template <int D>
+__global__ __launch_bounds__(QZ_THREADS) void quant_b32_kernel(QuantArgs a) {
+  constexpr int PER = 32 * D / 64;  // values per lane
+  constexpr int NV = PER / 8;       // 16-byte loads per lane
+  const long blk = (long)blockIdx.x * (QZ_THREADS / 64) + (threadIdx.x >> 6);
+  if (blk >= a.nblocks) return;
+  const int lane = threadIdx.x & 63;
+  const uint4* src = (const uint4*)(a.x + blk * 32 * D);
+  uint4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = src[i * 64 + lane];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const unsigned w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf16lo(w[j])), fabsf(bf16hi(w[j]))));
+  }
+  amax = wave_max(amax);
+  const float s = amax / 127.0f;  // correctly rounded division
+  if (lane == 0) a.scales[blk] = (amax == 0.f) ? 0.f : s;
+  uint2* dst = (uint2*)(a.codes + blk * 32 * D);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const unsigned w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    unsigned packed[2] = {0u, 0u};
+    if (amax != 0.f) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float q0 = fminf(fmaxf(rintf(bf16lo(w[j]) / s), -127.f), 127.f);
+        const float q1 = fminf(fmaxf(rintf(bf16hi(w[j]) / s), -127.f), 127.f);
+        const unsigned b0 = (unsigned)((int)q0) & 0xffu;
+        const unsigned b1 = (unsigned)((int)q1) & 0xffu;
+        packed[j >> 1] |= (b0 | (b1 << 8)) << (16 * (j & 1));
+      }
+    }
+    dst[i * 64 + lane] = make_uint2(packed[0], packed[1]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_b32(const QuantArgs& a, hipStream_t s) {
+  const long per_blk = QZ_THREADS / 64;
+  const int grid = (int)((a.nblocks + per_blk - 1) / per_blk);
+  if (grid == 0) return hipSuccess;
+  if (a.D == 128)
+    hipLaunchKernelGGL(quant_b32_kernel<128>, dim3(grid), dim3(QZ_THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL(quant_b32_kernel<64>, dim3(grid), dim3(QZ_THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace hsk

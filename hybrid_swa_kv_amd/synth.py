@@ -134,3 +134,24 @@ def from_torch_bf16(t) -> np.ndarray:
 
     bits = t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     return bf16_bits_to_f32(bits)
+
+
+def normal_gpu(workload: int, tensor_id: int, shape, outlier_p: float = 0.0, outlier_mult: float = 8.0,
+               device="cuda"):
+    """Seeded N(0,1) bf16 tensor drawn on the GPU (torch's Philox generator).
+
+    Same distribution as ``normal`` (float32 draw, optional outliers, one
+    round-to-nearest-even to bf16) but not the same values; used where only the
+    distribution matters (throughput runs), since drawing gigabytes on the host
+    is slow.
+    """
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(workload) * 1_000_003 + int(tensor_id) * 7919 + 12345)
+    x = torch.randn(tuple(int(s) for s in shape), generator=g, device=device, dtype=torch.float32)
+    if outlier_p > 0.0:
+        hit = torch.rand(x.shape, generator=g, device=device) < outlier_p
+        x = torch.where(hit, x * outlier_mult, x)
+        del hit
+    return x.to(torch.bfloat16)

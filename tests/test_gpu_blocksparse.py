@@ -1,0 +1,68 @@
+"""GPU parity: blocksparse_select_attend (bit-exact selection, attention within tolerance)."""
+
+import numpy as np
+import pytest
+import torch
+
+import hybrid_swa_kv_amd as hsk
+import oracle
+from hybrid_swa_kv_amd import synth
+from tests.helpers import bf16_excess, announce, f64, gpu_bf16, max_abs, out_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def check_selection(sel_gpu, q, k, block, topk, heads=None):
+    """Selected blocks must equal the oracle's; a difference is only accepted at a
+    provable near-tie (scores equal to within fp64 rounding of the dot product)."""
+    ref, scores = oracle.block_select(q, k, block, topk, heads=heads, return_scores=True)
+    heads = range(q.shape[1]) if heads is None else heads
+    for h in heads:
+        if np.array_equal(sel_gpu[h], ref[h]):
+            continue
+        for qb in np.nonzero((sel_gpu[h] != ref[h]).any(axis=1))[0]:
+            sc = scores[h][qb, :qb]
+            a, b = set(sel_gpu[h, qb][sel_gpu[h, qb] >= 0]), set(ref[h, qb][ref[h, qb] >= 0])
+            assert len(a) == len(b) == min(qb, topk), (h, qb)
+            cut = np.sort(sc)[::-1][topk - 1]
+            tol = 1e-12 * max(1.0, float(np.max(np.abs(sc))))
+            for kb in a ^ b:
+                assert abs(sc[kb] - cut) <= tol, ("selection differs away from a tie", h, qb, kb)
+
+
+@pytest.mark.parametrize("L,Hq,Hkv,D,topk,window", [
+    (1024, 4, 1, 128, 4, 100), (2048, 8, 2, 128, 8, 1024), (4096, 4, 1, 64, 64, 1024),
+    (1024, 2, 2, 128, 0, 64), (640, 4, 2, 128, 256, 64), (2048, 4, 1, 128, 3, 4096)])
+def test_blocksparse_parity(L, Hq, Hkv, D, topk, window):
+    announce("blocksparse", L=L, Hq=Hq, Hkv=Hkv, D=D, topk=topk, window=window)
+    seed = 90 + L + topk
+    q = synth.token_major(seed, synth.Q, L, Hq, D)
+    k = synth.token_major(seed, synth.K, L, Hkv, D)
+    v = synth.token_major(seed, synth.V, L, Hkv, D)
+    out, sel = hsk.blocksparse_select_attend(gpu_bf16(q), gpu_bf16(k), gpu_bf16(v), 64, topk, window)
+    torch.cuda.synchronize()
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    if topk > 0:
+        sel_np = sel.cpu().numpy()
+        check_selection(sel_np, qf, kf, 64, topk)
+    else:
+        sel_np = np.zeros((Hq, L // 64, 0), dtype=np.int32)
+    ref = oracle.blocksparse_attend(qf, kf, vf, sel_np, 64, window)
+    ex = bf16_excess(out_f64(out), ref)
+    assert ex <= 0, (ex, max_abs(out_f64(out), ref))
+
+
+def test_blocksparse_exact_tie():
+    # duplicate key blocks produce exactly equal scores: the lower block must win
+    L, Hq, Hkv, D, topk = 1024, 2, 1, 128, 2
+    announce("blocksparse_tie")
+    q = synth.token_major(95, synth.Q, L, Hq, D)
+    k = synth.token_major(95, synth.K, L, Hkv, D).copy()
+    v = synth.token_major(95, synth.V, L, Hkv, D)
+    for src, dst in ((1, 5), (2, 9), (1, 12)):
+        k[64 * dst: 64 * dst + 64] = k[64 * src: 64 * src + 64]
+    out, sel = hsk.blocksparse_select_attend(gpu_bf16(q), gpu_bf16(k), gpu_bf16(v), 64, topk, 64)
+    ref_sel = oracle.block_select(f64(q), f64(k), 64, topk)
+    assert np.array_equal(sel.cpu().numpy(), ref_sel)
+    ref = oracle.blocksparse_attend(f64(q), f64(k), f64(v), ref_sel, 64, 64)
+    assert bf16_excess(out_f64(out), ref) <= 0
