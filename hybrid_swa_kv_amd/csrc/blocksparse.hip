@@ -196,7 +196,7 @@ __global__ __launch_bounds__(AT_THREADS) void bs_attend_kernel(BlockSparseArgs a
   const int ntiles = npre + (qb - kw0 + 1);  // then the window's blocks kw0 .. qb
 
   const int lane = __lane_id();
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
   const int r0 = q0 + 32 * w;
   const int row = r0 + (lane & 31);
   FlashWave<D> fw;

@@ -6,7 +6,9 @@
 //      B = the wave's Q fragment held in registers for the whole loop), so lane l
 //      holds 32 scores of query row l%32 and lane l^32 the other 32;
 //   2. masks edge tiles, runs the online softmax in the log2 domain (row max via
-//      one permlane32 swap, v_exp_f32), rescales the accumulator;
+//      one permlane32 swap, v_exp_f32 on fma(s, scale*log2e, -m)); the offset m
+//      and the accumulator are only rescaled when a row maximum grows by > 2^8,
+//      and the row sum is taken with v_dot2_f32_bf16 on the packed bf16 P;
 //   3. accumulates O^T += V^T * P^T: P^T is the softmax output in place (its key
 //      order is matched by the V^T operand), V^T comes from LDS through two
 //      ds_read_b64_tr_b16 per MFMA.
@@ -27,8 +29,15 @@ struct FtCfg {
   static constexpr int DB = D / 32;          // 32-row d blocks of O^T
 };
 
+// Chunk swizzle.  D = 128 (16 chunks of 16 B per row): 16 consecutive rows read at
+// one logical chunk land on 16 different chunks (the K operand reads), and the 4
+// consecutive rows of one transpose read keep an aligned group of 4 chunks on 4
+// disjoint groups (the V^T reads).  D = 64 (8 chunks): the same idea on 3 bits.
 template <int NCH>
-__device__ __forceinline__ int ft_swz(int row) { return (2 * (row & 7)) & (NCH - 1); }
+__device__ __forceinline__ int ft_swz(int row) {
+  if (NCH == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return ((row & 1) << 2) | ((row >> 1) & 3);
+}
 
 template <int NCH>
 __device__ __forceinline__ int ft_off(int row, int chunk) {
@@ -45,14 +54,25 @@ struct TileStage {
   // rows kt*64 .. kt*64+63 of kbase/vbase (row stride in elements); rows >= nrows read as 0
   __device__ __forceinline__ void load(const uint16_t* kbase, const uint16_t* vbase, size_t stride,
                                        int kt, int nrows) {
+    const size_t tile_off = (size_t)kt * FT_BN * stride;
+    if ((kt + 1) * FT_BN <= nrows) {  // whole tile in range (uniform)
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int u = i * NT + (int)threadIdx.x;
+        const size_t off = tile_off + (size_t)(u / C::NCH) * stride + (u % C::NCH) * 8;
+        kreg[i] = *(const uint4*)(kbase + off);
+        vreg[i] = *(const uint4*)(vbase + off);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int u = i * NT + (int)threadIdx.x;
       const int r = u / C::NCH, c = u % C::NCH;
-      const int kp = kt * FT_BN + r;
-      if (kp < nrows) {
-        kreg[i] = *(const uint4*)(kbase + (size_t)kp * stride + c * 8);
-        vreg[i] = *(const uint4*)(vbase + (size_t)kp * stride + c * 8);
+      if (kt * FT_BN + r < nrows) {
+        const size_t off = tile_off + (size_t)r * stride + c * 8;
+        kreg[i] = *(const uint4*)(kbase + off);
+        vreg[i] = *(const uint4*)(vbase + off);
       } else {
         kreg[i] = make_uint4(0, 0, 0, 0);
         vreg[i] = make_uint4(0, 0, 0, 0);
@@ -119,48 +139,62 @@ struct FlashWave {
         s[sub] = mfma32(ka, qf[c], s[sub]);
       }
     }
+    if (__builtin_expect(need_mask, 0)) {  // edge tile (wave-uniform branch)
+      // key of register r: k0 + 32 sub + 8 (r/4) + 4 (lane/32) + r%4
+      const int d0 = row - k0 - 4 * (lane >> 5);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int dd = d0 - 32 * sub - 8 * (r >> 2) - (r & 3);
+          if ((unsigned)dd >= (unsigned)W) s[sub][r] = kNegInf;
+        }
+    }
     float mx = kNegInf;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[sub][r] * scale_log2;
-        if (need_mask) {
-          const int kp = k0 + 32 * sub + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int dd = row - kp;
-          if (dd < 0 || dd >= W) x = kNegInf;
-        }
-        s[sub][r] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
     mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m, mx);
-    const float base = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m - base);
-    float ps = 0.f;
+    // Lazy rescale: the exponent offset m only moves when a row's maximum grows
+    // by more than 8 (a factor 256), so most tiles skip the accumulator rescale.
+    // Exact after the final division: numerator and denominator share m.
+    const float mts = mx * scale_log2;
+    if (__any(mts > m + 8.f)) {
+      const float m_new = fmaxf(m, mts);
+      const float alpha = (m == kNegInf) ? 0.f : fast_exp2(m - m_new);
+      l *= alpha;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+      for (int d = 0; d < C::DB; ++d)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(s[sub][r] - base);
-        s[sub][r] = p;
-        ps += p;
+        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+      m = m_new;
+    }
+    const float negm = (m == kNegInf) ? 0.f : -m;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    u32x4 pw[4];
+#pragma unroll
+    for (int kap = 0; kap < 4; ++kap) {
+      const int sub = kap >> 1, half = kap & 1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = fast_exp2(fmaf(s[sub][8 * half + 2 * j], scale_log2, negm));
+        const float p1 = fast_exp2(fmaf(s[sub][8 * half + 2 * j + 1], scale_log2, negm));
+        bf16x2 pp;
+        pp[0] = (__bf16)p0;
+        pp[1] = (__bf16)p1;
+        pw[kap][j] = __builtin_bit_cast(unsigned, pp);
+        // the normaliser sums the same bf16-rounded probabilities the MFMA uses
+        // (the pair is kept as its own value: bit-casting a u32x4 element here
+        // made hipcc reuse element 0 for every j)
+        l = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l, false);
       }
-    l = l * alpha + ps;
-    m = m_new;
-#pragma unroll
-    for (int d = 0; d < C::DB; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+    }
 
     const int gq = lane >> 4, sl = lane & 15;
 #pragma unroll
     for (int kap = 0; kap < 4; ++kap) {
-      const int sub = kap >> 1, half = kap & 1;
-      u32x4 pw;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pw[j] = pack_bf16x2(s[sub][8 * half + 2 * j], s[sub][8 * half + 2 * j + 1]);
-      const bf16x8 pb = as_bf16x8(pw);
+      const bf16x8 pb = as_bf16x8(pw[kap]);
       // k-slot j of lane group gq/2 <-> key 16 kap + 4 (gq/2) + j (j < 4) or + 8 + (j - 4)
       const int kr = 16 * kap + 4 * (gq >> 1) + (sl >> 2);
 #pragma unroll

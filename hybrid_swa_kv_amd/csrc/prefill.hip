@@ -43,7 +43,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(PrefillArgs
   const int W = a.window;           // >= 1; full causal is passed as a window > L
   const int q0 = qblk * PF_BM;
   const int lane = __lane_id();
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
   const int r0 = q0 + 32 * w;        // first row of this wave
   const int row = r0 + (lane & 31);  // this lane's query row
 

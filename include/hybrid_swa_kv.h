@@ -68,6 +68,7 @@ int hsk_abi_version(void);
  * k,v [B, L, Hkv, D]  dtype
  * out [B, L, Hq,  D]  dtype, written
  * dtype HSK_BF16 (MFMA path) or HSK_F32 (exact-fp32 path, any L, for small cases).
+ * scale > 0 (the softmax scale, usually 1/sqrt(D)).
  * ring_k, ring_v: optional (both NULL or both set), [B, Hkv, ring_w, D] dtype.
  *   When set, the K/V of positions max(0, L - ring_w) .. L-1 are also copied to
  *   slot (position mod ring_w), the sliding-window pool of [MiMo-inf] section 2
@@ -163,7 +164,7 @@ size_t attn_decode_int8kv_workspace_size(int B, int Hq, int Hkv, int D, int T8, 
  *
  * q   [L, Hq,  D] bf16;  k, v [L, Hkv, D] bf16;  out [L, Hq, D] bf16, written
  * sel [Hq, L/block, topk] int32, written
- * block == 64;  L % block == 0;  0 <= topk <= 256;  window >= 1.
+ * block == 64;  L % block == 0;  0 <= topk <= 256;  window >= 1;  scale > 0.
  * workspace: blocksparse_workspace_size(...) bytes (block means, fp64).
  */
 int blocksparse_select_attend(const void* q, const void* k, const void* v, void* out,

@@ -54,6 +54,7 @@ def test_prefill_validation(lib):
     assert f(P, P, P, P, 1, 8, 2, 2, 96, 0, 1.0, 1, None, None, 0, None) == UNSUP
     assert f(P, P, P, P, 1, 8, 2, 2, 128, 0, 1.0, 7, None, None, 0, None) == UNSUP
     assert f(P, P, P, P, 1, 8, 2, 2, 128, 0, float("nan"), 1, None, None, 0, None) == SHAPE
+    assert f(P, P, P, P, 1, 8, 2, 2, 128, 0, -1.0, 1, None, None, 0, None) == SHAPE
     assert f(P, P, P, P, 1, 8, 2, 2, 128, 0, 1.0, 1, P, P, 0, None) == SHAPE
     assert f(P, MIS, P, P, 1, 8, 2, 2, 128, 0, 1.0, 1, None, None, 0, None) == ALIGN
 
