@@ -97,6 +97,7 @@ int swa_decode_ring(const void* q, const void* k_new, const void* v_new, void* r
   if (!q || !k_new || !v_new || !ring_k || !ring_v || !pos || !out) return HSK_ERR_NULL;
   if (B <= 0 || W <= 0 || W > 65536) return HSK_ERR_SHAPE;
   if (int rc = check_heads(Hq, Hkv, D)) return rc;
+  if (Hq / Hkv > 16 && (Hq / Hkv) % 16 != 0) return HSK_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return HSK_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(ring_k) ||
       !aligned16(ring_v) || !aligned16(out) || !aligned4(pos) || (slot_out && !aligned4(slot_out)))

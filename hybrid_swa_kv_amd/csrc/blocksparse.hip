@@ -17,6 +17,8 @@
 //                (query head, query block); key tiles are the selected blocks
 //                before the window followed by the window's blocks; selected
 //                tiles need no mask, window tiles use the sliding-window mask.
+//                A single LDS tile buffer (next tile staged in registers) keeps
+//                four workgroups resident per CU.
 #include "common.hpp"
 #include "flash_tile.hpp"
 #include "kernels.hpp"
@@ -68,8 +70,8 @@ __device__ __forceinline__ unsigned long long order_key(double x) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// grid: Hkv * nb * (G / hpw)
-template <int HPW>
+// grid: Hkv * nb * (G / hpw); MAXG * 64 >= nb (key groups held per lane)
+template <int HPW, int MAXG>
 __global__ __launch_bounds__(SEL_THREADS) void bs_select_kernel(BlockSparseArgs a) {
   __shared__ double qs[256][HPW];               // query block means, [d][head]
   extern __shared__ double sc_dyn[];            // scores, [head][nb]
@@ -114,33 +116,40 @@ __global__ __launch_bounds__(SEL_THREADS) void bs_select_kernel(BlockSparseArgs 
     for (int i = lane; i < topk; i += 64) out[i] = (i < n) ? i : -1;
     return;
   }
-  // top-k threshold: largest T with #{key >= T} >= topk
-  unsigned long long T = 0;
+  // top-k threshold: the largest T with #{key >= T} >= topk, found bit by bit.
+  // Each lane keeps its keys (blocks lane, lane+64, ...) in registers; a wave
+  // ballot + popcount counts them, so no step needs a cross-lane reduction.
   const int ngr = (n + 63) >> 6;
+  unsigned long long keys[MAXG];
+#pragma unroll
+  for (int i = 0; i < MAXG; ++i) {
+    const int kb = i * 64 + lane;
+    keys[i] = (i < ngr && kb < n) ? order_key(sc_dyn[(size_t)w * a.nb + kb]) : 0ull;
+  }
+  // absent slots hold key 0, which sorts below every real key
+  unsigned long long T = 0;
   for (int bit = 63; bit >= 0; --bit) {
     const unsigned long long cand = T | (1ull << bit);
     int cnt = 0;
-    for (int i = 0; i < ngr; ++i) {
-      const int kb = i * 64 + lane;
-      if (kb < n && order_key(sc_dyn[(size_t)w * a.nb + kb]) >= cand) ++cnt;
-    }
-    const float tot = wave_sum((float)cnt);
-    if (tot >= (float)topk) T = cand;
+#pragma unroll
+    for (int i = 0; i < MAXG; ++i)
+      if (i < ngr) cnt += __popcll(__ballot(keys[i] >= cand));
+    if (cnt >= topk) T = cand;
   }
   int gt = 0;
-  for (int i = 0; i < ngr; ++i) {
-    const int kb = i * 64 + lane;
-    if (kb < n && order_key(sc_dyn[(size_t)w * a.nb + kb]) > T) ++gt;
-  }
-  const int need = topk - (int)wave_sum((float)gt);
+#pragma unroll
+  for (int i = 0; i < MAXG; ++i)
+    if (i < ngr) gt += __popcll(__ballot(keys[i] > T));
+  const int need = topk - gt;
   const unsigned long long lt_mask = (1ull << lane) - 1ull;
   int eq_before = 0, written = 0;
-  for (int i = 0; i < ngr; ++i) {
+#pragma unroll
+  for (int i = 0; i < MAXG; ++i) {
+    if (i >= ngr) continue;
     const int kb = i * 64 + lane;
-    const unsigned long long key = (kb < n) ? order_key(sc_dyn[(size_t)w * a.nb + kb]) : 0ull;
     const bool valid = kb < n;
-    const bool is_gt = valid && key > T;
-    const bool is_eq = valid && key == T;
+    const bool is_gt = valid && keys[i] > T;
+    const bool is_eq = valid && keys[i] == T;
     const unsigned long long eqb = __ballot(is_eq);
     const int rank = eq_before + __popcll(eqb & lt_mask);
     const bool take = is_gt || (is_eq && rank < need);
@@ -152,18 +161,21 @@ __global__ __launch_bounds__(SEL_THREADS) void bs_select_kernel(BlockSparseArgs 
   for (int i = written + lane; i < topk; i += 64) out[i] = -1;
 }
 
-// grid: Hq * nb, XCD-aware (see prefill)
+// grid: Hq * nb
 template <int D>
 __global__ __launch_bounds__(AT_THREADS) void bs_attend_kernel(BlockSparseArgs a) {
   using C = FtCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * C::TILE];
+  // one K/V tile buffer (33 KB with the lists): four workgroups fit per CU
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::TILE];
   __shared__ int list[256];                  // selected blocks before the window
   __shared__ unsigned selbits[SEL_MAXNB / 32];
   __shared__ int s_npre;
 
+  // KV-head-major order across the whole chip: the workgroups in flight share
+  // one KV head, whose K/V (67 MB at 131072 x 128) stays in the 256 MB MALL;
+  // the selected blocks are scattered, so reuse comes from the MALL, not L2.
   const int total = a.Hq * a.nb;
-  const int per = gridDim.x >> 3;
-  const int nlin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  const int nlin = blockIdx.x;
   if (nlin >= total) return;
   const int G = a.Hq / a.Hkv;
   const int hh = nlin % G;
@@ -210,13 +222,15 @@ __global__ __launch_bounds__(AT_THREADS) void bs_attend_kernel(BlockSparseArgs a
   stg.load(kbase, vbase, stride, tile_of(0), L);
   stg.store(smem);
   for (int it = 0; it < ntiles; ++it) {
-    __syncthreads();
+    __syncthreads();                         // tile it visible
     const int kt = tile_of(it);
     if (it + 1 < ntiles) stg.load(kbase, vbase, stride, tile_of(it + 1), L);
-    const char* ks = smem + (it & 1) * 2 * C::TILE;
     const bool full = (selbits[kt >> 5] >> (kt & 31)) & 1u;
-    fw.tile(ks, ks + C::TILE, kt * FT_BN, r0, row, W, full, a.scale_log2);
-    if (it + 1 < ntiles) stg.store(smem + ((it + 1) & 1) * 2 * C::TILE);
+    fw.tile(smem, smem + C::TILE, kt * FT_BN, r0, row, W, full, a.scale_log2);
+    if (it + 1 < ntiles) {
+      __syncthreads();                       // every wave is done reading tile it
+      stg.store(smem);
+    }
   }
   fw.store(a.out + ((size_t)row * a.Hq + h) * D);
 }
@@ -229,14 +243,19 @@ hipError_t launch_blocksparse(const BlockSparseArgs& a, hipStream_t s) {
   const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
   const int sgrid = a.topk > 0 ? a.Hkv * a.nb * (G / hpw) : 0;
   const size_t dyn = (size_t)hpw * a.nb * sizeof(double);
+  const bool big = a.nb > 2048;
   if (sgrid == 0) {
     // no long-range blocks: the attention below is the sliding window alone
-  } else if (hpw == 4)
-    hipLaunchKernelGGL(bs_select_kernel<4>, dim3(sgrid), dim3(SEL_THREADS), dyn, s, a);
-  else if (hpw == 2)
-    hipLaunchKernelGGL(bs_select_kernel<2>, dim3(sgrid), dim3(SEL_THREADS), dyn, s, a);
-  else
-    hipLaunchKernelGGL(bs_select_kernel<1>, dim3(sgrid), dim3(SEL_THREADS), dyn, s, a);
+  } else if (hpw == 4) {
+    if (big) hipLaunchKernelGGL((bs_select_kernel<4, 64>), dim3(sgrid), dim3(SEL_THREADS), dyn, s, a);
+    else hipLaunchKernelGGL((bs_select_kernel<4, 32>), dim3(sgrid), dim3(SEL_THREADS), dyn, s, a);
+  } else if (hpw == 2) {
+    if (big) hipLaunchKernelGGL((bs_select_kernel<2, 64>), dim3(sgrid), dim3(SEL_THREADS), dyn, s, a);
+    else hipLaunchKernelGGL((bs_select_kernel<2, 32>), dim3(sgrid), dim3(SEL_THREADS), dyn, s, a);
+  } else {
+    if (big) hipLaunchKernelGGL((bs_select_kernel<1, 64>), dim3(sgrid), dim3(SEL_THREADS), dyn, s, a);
+    else hipLaunchKernelGGL((bs_select_kernel<1, 32>), dim3(sgrid), dim3(SEL_THREADS), dyn, s, a);
+  }
   const int total = a.Hq * a.nb;
   const int grid = (total + 7) / 8 * 8;
   if (a.D == 128)

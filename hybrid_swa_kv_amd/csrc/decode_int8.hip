@@ -14,6 +14,7 @@
 // Partial (max, sum, acc) records of the 4 waves are merged in LDS and written
 // to the workspace; a second kernel merges the splits in a fixed order.
 #include "common.hpp"
+#include "decode_mfma.hpp"
 #include "kernels.hpp"
 
 namespace hsk {
@@ -22,151 +23,8 @@ namespace {
 
 constexpr int DQ_THREADS = 256;
 
-__device__ __forceinline__ float i8(unsigned w, int byte) {
-  return (float)(int)(signed char)(w >> (8 * byte));
-}
-
-// 16 int8 codes -> two bf16x8 operands (codes 0..7, 8..15)
-__device__ __forceinline__ void cvt16(uint4 c, bf16x8& lo, bf16x8& hi) {
-  u32x4 a, b;
-  a[0] = pack_bf16x2(i8(c.x, 0), i8(c.x, 1));
-  a[1] = pack_bf16x2(i8(c.x, 2), i8(c.x, 3));
-  a[2] = pack_bf16x2(i8(c.y, 0), i8(c.y, 1));
-  a[3] = pack_bf16x2(i8(c.y, 2), i8(c.y, 3));
-  b[0] = pack_bf16x2(i8(c.z, 0), i8(c.z, 1));
-  b[1] = pack_bf16x2(i8(c.z, 2), i8(c.z, 3));
-  b[2] = pack_bf16x2(i8(c.w, 0), i8(c.w, 1));
-  b[3] = pack_bf16x2(i8(c.w, 2), i8(c.w, 3));
-  lo = as_bf16x8(a);
-  hi = as_bf16x8(b);
-}
-
-template <int D>
-struct WaveState {
-  static constexpr int NH = D / 64;
-  f32x4 o[NH][4];
-  float m, l;
-};
-
-// One 32-token chunk starting at row c0 of the region; rows >= rend are masked.
-// key of P^T slot j (of lane group gq): 16 (j/4) + 4 gq + j%4
-template <int D, bool INT8>
-__device__ __forceinline__ void chunk(WaveState<D>& st, const bf16x8 (&qb)[D / 64][2],
-                                      const void* kbase, const void* vbase, int c0, int rend,
-                                      float sk, float sv, int lane) {
-  constexpr int NK = D / 64;
-  const int hl = lane & 15, gq = lane >> 4;
-  f32x4 s[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s[t][r] = 0.f;
-    const int row = c0 + 16 * t + hl;
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      bf16x8 a0, a1;
-      if (INT8) {
-        const uint4 raw = *(const uint4*)((const int8_t*)kbase + (size_t)row * D + 64 * kk + 16 * gq);
-        cvt16(raw, a0, a1);
-      } else {
-        uint4 r0 = make_uint4(0, 0, 0, 0), r1 = r0;
-        if (row < rend) {
-          const uint16_t* p = (const uint16_t*)kbase + (size_t)row * D + 64 * kk + 16 * gq;
-          r0 = *(const uint4*)p;
-          r1 = *(const uint4*)(p + 8);
-        }
-        a0 = as_bf16x8(r0);
-        a1 = as_bf16x8(r1);
-      }
-      s[t] = mfma16(a0, qb[kk][0], s[t]);
-      s[t] = mfma16(a1, qb[kk][1], s[t]);
-    }
-  }
-  // V^T operands, loaded before the softmax so the loads overlap it
-  bf16x8 va[NK][4];
-#pragma unroll
-  for (int hv = 0; hv < NK; ++hv) {
-    if (INT8) {
-      unsigned rw[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = c0 + 16 * (j >> 2) + 4 * gq + (j & 3);
-        rw[j] = *(const unsigned*)((const int8_t*)vbase + (size_t)row * D + 64 * hv + 4 * hl);
-      }
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        u32x4 t;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) t[q] = pack_bf16x2(i8(rw[2 * q], jj), i8(rw[2 * q + 1], jj));
-        va[hv][jj] = as_bf16x8(t);
-      }
-    } else {
-      uint2 rw[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = c0 + 16 * (j >> 2) + 4 * gq + (j & 3);
-        rw[j] = make_uint2(0, 0);
-        if (row < rend) rw[j] = *(const uint2*)((const uint16_t*)vbase + (size_t)row * D + 64 * hv + 4 * hl);
-      }
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        u32x4 t;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const unsigned x0 = (jj < 2) ? rw[2 * q].x : rw[2 * q].y;
-          const unsigned x1 = (jj < 2) ? rw[2 * q + 1].x : rw[2 * q + 1].y;
-          // low or high bf16 of each dword -> one packed pair
-          t[q] = (jj & 1) ? __builtin_amdgcn_perm(x1, x0, 0x07060302u)
-                          : __builtin_amdgcn_perm(x1, x0, 0x05040100u);
-        }
-        va[hv][jj] = as_bf16x8(t);
-      }
-    }
-  }
-  float x[8];
-  float mx = kNegInf;
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v = s[t][r] * sk;
-      if (!INT8 && c0 + 16 * t + 4 * gq + r >= rend) v = kNegInf;
-      x[4 * t + r] = v;
-      mx = fmaxf(mx, v);
-    }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, xor32(mx));
-  const float m_new = fmaxf(st.m, mx);
-  const float base = (m_new == kNegInf) ? 0.f : m_new;
-  const float alpha = fast_exp2(st.m - base);
-  // P is rounded to bf16 for the MFMA; the normaliser sums the same rounded
-  // values, so a row dominated by one key returns that key's value exactly.
-  float ps = 0.f;
-  u32x4 pw;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float p0 = fast_exp2(x[2 * q] - base), p1 = fast_exp2(x[2 * q + 1] - base);
-    pw[q] = pack_bf16x2(p0, p1);
-    ps += bf16lo(pw[q]) + bf16hi(pw[q]);
-  }
-  st.l = st.l * alpha + ps;
-  st.m = m_new;
-  const bf16x8 pb = as_bf16x8(pw);
-  // the chunk's V scale (1 for bf16 rows) multiplies its fresh partial product once
-#pragma unroll
-  for (int hv = 0; hv < NK; ++hv)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      f32x4 part = {0.f, 0.f, 0.f, 0.f};
-      part = mfma16(va[hv][jj], pb, part);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st.o[hv][jj][r] = fmaf(st.o[hv][jj][r], alpha, sv * part[r]);
-    }
-}
-
 template <int D>
 __global__ __launch_bounds__(DQ_THREADS) void int8_decode_kernel(Int8DecodeArgs a) {
-  constexpr int NK = D / 64;
   __shared__ float sm_m[4][16], sm_l[4][16];
   __shared__ float sm_o[4][16][D];
 
@@ -175,80 +33,44 @@ __global__ __launch_bounds__(DQ_THREADS) void int8_decode_kernel(Int8DecodeArgs 
   const int unit = blockIdx.x / nsplit;  // b * Hkv + g
   const int g = unit % a.Hkv, b = unit / a.Hkv;
   const int G = a.Hq / a.Hkv;
-  const int lane = __lane_id(), w = threadIdx.x >> 6;
-  const int hl = lane & 15, gq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  bf16x8 qb[NK][2];
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk)
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      uint4 t = make_uint4(0, 0, 0, 0);
-      if (hl < G) t = *(const uint4*)(a.q + ((size_t)b * a.Hq + g * G + hl) * D + 64 * kk + 16 * gq + 8 * e);
-      qb[kk][e] = as_bf16x8(t);
-    }
-
-  WaveState<D> st;
-#pragma unroll
-  for (int hv = 0; hv < NK; ++hv)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st.o[hv][jj][r] = 0.f;
-  st.m = kNegInf;
-  st.l = 0.f;
+  DecodeWave<D> st;
+  st.init(a.q + ((size_t)b * a.Hq + g * G) * D, G);
 
   if (split < a.ns8) {
     const int tok0 = split * a.split8;
     const int tok1 = min(a.T8, tok0 + a.split8);
-    const int8_t* kc = a.kc + (size_t)unit * a.T8 * D;
-    const int8_t* vc = a.vc + (size_t)unit * a.T8 * D;
+    const Int8Rows<D> rows{a.kc + (size_t)unit * a.T8 * D, a.vc + (size_t)unit * a.T8 * D};
     const float* ks = a.ks + (size_t)unit * (a.T8 / 32);
     const float* vs = a.vs + (size_t)unit * (a.T8 / 32);
-    for (int c0 = tok0 + 32 * w; c0 < tok1; c0 += 128) {
-      const float sk = ks[c0 >> 5] * a.scale_log2;
-      const float sv = vs[c0 >> 5];
-      chunk<D, true>(st, qb, kc, vc, c0, tok1, sk, sv, lane);
+    // two chunks in flight: the next chunk's loads are issued before this one's math
+    int c0 = tok0 + 32 * w;
+    if (c0 < tok1) {
+      typename DecodeWave<D>::template Raw<true> cur, nxt;
+      st.template load<true>(rows, c0, cur);
+      for (; c0 < tok1; c0 += 128) {
+        const bool more = c0 + 128 < tok1;
+        if (more) st.template load<true>(rows, c0 + 128, nxt);
+        st.template compute<true>(rows, c0, cur, ks[c0 >> 5] * a.scale_log2, vs[c0 >> 5]);
+        if (more) cur = nxt;
+      }
     }
   } else {
     const int tok0 = (split - a.ns8) * a.splith;
     const int tok1 = min(a.Th, tok0 + a.splith);
-    const uint16_t* kh = a.kh + (size_t)unit * a.Th * D;
-    const uint16_t* vh = a.vh + (size_t)unit * a.Th * D;
-    for (int c0 = tok0 + 32 * w; c0 < tok1; c0 += 128)
-      chunk<D, false>(st, qb, kh, vh, c0, tok1, a.scale_log2, 1.f, lane);
+    const Bf16Rows<D> rows{a.kh + (size_t)unit * a.Th * D, a.vh + (size_t)unit * a.Th * D, tok1};
+    for (int c0 = tok0 + 32 * w; c0 < tok1; c0 += 128) st.template chunk<false>(rows, c0, a.scale_log2, 1.f);
   }
 
-  // merge the four waves of this workgroup
-  float lsum = st.l;
-  lsum += __shfl_xor(lsum, 16);
-  lsum += xor32(lsum);
-  if (hl < G) {
-#pragma unroll
-    for (int hv = 0; hv < NK; ++hv)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm_o[w][hl][64 * hv + 16 * gq + 4 * r + jj] = st.o[hv][jj][r];
-    if (gq == 0) {
-      sm_m[w][hl] = st.m;
-      sm_l[w][hl] = lsum;
-    }
-  }
+  // merge the four waves of this workgroup into one split record
+  st.stash(sm_m, sm_l, sm_o, w, G);
   __syncthreads();
   float* rec0 = a.ws + ((size_t)unit * nsplit + split) * G * (D + 2);
   for (int e = threadIdx.x; e < G * D; e += DQ_THREADS) {
     const int head = e / D, d = e % D;
-    float M = kNegInf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) M = fmaxf(M, sm_m[i][head]);
-    float O = 0.f, Ls = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float f = (sm_m[i][head] == kNegInf) ? 0.f : fast_exp2(sm_m[i][head] - M);
-      O += f * sm_o[i][head][d];
-      Ls += f * sm_l[i][head];
-    }
+    float M, Ls;
+    const float O = merge_waves<4, D>(sm_m, sm_l, sm_o, head, d, M, Ls);
     float* rec = rec0 + (size_t)head * (D + 2);
     rec[d] = O;
     if (d == 0) {
@@ -259,27 +81,57 @@ __global__ __launch_bounds__(DQ_THREADS) void int8_decode_kernel(Int8DecodeArgs 
 }
 
 // merge split records in split order: out = sum 2^(m_i - M) acc_i / sum 2^(m_i - M) l_i
+// One workgroup per (sequence, query head); split weights go through LDS so the
+// per-d loop issues independent loads.
 template <int D>
 __global__ __launch_bounds__(D) void int8_combine_kernel(Int8DecodeArgs a) {
+  constexpr int CH = 256;  // splits weighed per pass
+  __shared__ float sf[CH];
+  __shared__ float red[D / 64];
+  __shared__ float s_M, s_L;
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int G = a.Hq / a.Hkv;
   const int unit = b * a.Hkv + h / G, head = h % G;
   const int nsplit = a.ns8 + a.nsh;
-  const int d = threadIdx.x;
+  const int t = threadIdx.x;
   const float* base = a.ws + (size_t)unit * nsplit * G * (D + 2) + (size_t)head * (D + 2);
   const size_t stride = (size_t)G * (D + 2);
-  float M = kNegInf;
-  for (int i = 0; i < nsplit; ++i) M = fmaxf(M, base[i * stride + D]);
-  float O = 0.f, Ls = 0.f;
-  for (int i = 0; i < nsplit; ++i) {
-    const float* rec = base + i * stride;
-    const float mi = rec[D];
-    const float f = (mi == kNegInf) ? 0.f : fast_exp2(mi - M);
-    O += f * rec[d];
-    Ls += f * rec[D + 1];
+  float mx = kNegInf;
+  for (int i = t; i < nsplit; i += D) mx = fmaxf(mx, base[i * stride + D]);
+  mx = wave_max(mx);
+  if ((t & 63) == 0) red[t >> 6] = mx;
+  __syncthreads();
+  if (t == 0) {
+    float M = kNegInf;
+    for (int i = 0; i < D / 64; ++i) M = fmaxf(M, red[i]);
+    s_M = M;
+    s_L = 0.f;
   }
-  a.out[((size_t)b * a.Hq + h) * D + d] = f32_to_bf16(O / Ls);
+  __syncthreads();
+  const float M = s_M;
+  float O = 0.f, Lpart = 0.f;
+  for (int c0 = 0; c0 < nsplit; c0 += CH) {
+    const int n = min(CH, nsplit - c0);
+    for (int i = t; i < n; i += D) {
+      const float* rec = base + (size_t)(c0 + i) * stride;
+      const float mi = rec[D];
+      const float f = (mi == kNegInf) ? 0.f : fast_exp2(mi - M);
+      sf[i] = f;
+      Lpart += f * rec[D + 1];
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int i = 0; i < n; ++i) O += sf[i] * base[(size_t)(c0 + i) * stride + t];
+    __syncthreads();
+  }
+  Lpart = wave_sum(Lpart);
+  if ((t & 63) == 0) red[t >> 6] = Lpart;
+  __syncthreads();
+  float L = 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) L += red[i];
+  a.out[((size_t)b * a.Hq + h) * D + t] = f32_to_bf16(O / L);
 }
 
 }  // namespace

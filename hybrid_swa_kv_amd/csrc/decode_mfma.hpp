@@ -1,0 +1,350 @@
+// One-token decode on v_mfma_f32_16x16x32_bf16, shared by the ring decode and
+// the INT8 + bf16 decode.
+//
+// A wave processes 32-key chunks with the (up to 16) query heads of one KV head
+// on the MFMA N axis; lane l serves head l%16 (zero query for unused heads) and
+// lane group g = l/16:
+//   S   = K * q^T      A = K rows (16 keys x 32 d), B = q^T
+//                      -> lane l holds the scores of keys 16t + 4g + r (t<2, r<4)
+//   O^T += V^T * P^T   A = V^T (16 d x 32 keys), B = P^T: a lane's 8 probabilities
+//                      are exactly its B operand, in the key order of its scores;
+//                      the V^T operand takes, for its lane's d, the same 8 keys:
+//                      each lane reads 4 adjacent d from 8 rows and the packing
+//                      order performs the transpose.
+// Output: lane l holds O[head l%16][64 hv + 16 g + 4 r + jj] for the tile (hv, jj).
+// INT8 rows are converted exactly to bf16 in registers (|code| <= 127); the K
+// scale multiplies the chunk's scores, the V scale the chunk's PV partial.
+#pragma once
+
+#include "common.hpp"
+
+namespace hsk {
+
+__device__ __forceinline__ float i8(unsigned w, int byte) {
+  return (float)(int)(signed char)(w >> (8 * byte));
+}
+
+// 16 int8 codes -> two bf16x8 operands (codes 0..7, 8..15)
+__device__ __forceinline__ void cvt16(uint4 c, bf16x8& lo, bf16x8& hi) {
+  u32x4 a, b;
+  a[0] = pack_bf16x2(i8(c.x, 0), i8(c.x, 1));
+  a[1] = pack_bf16x2(i8(c.x, 2), i8(c.x, 3));
+  a[2] = pack_bf16x2(i8(c.y, 0), i8(c.y, 1));
+  a[3] = pack_bf16x2(i8(c.y, 2), i8(c.y, 3));
+  b[0] = pack_bf16x2(i8(c.z, 0), i8(c.z, 1));
+  b[1] = pack_bf16x2(i8(c.z, 2), i8(c.z, 3));
+  b[2] = pack_bf16x2(i8(c.w, 0), i8(c.w, 1));
+  b[3] = pack_bf16x2(i8(c.w, 2), i8(c.w, 3));
+  lo = as_bf16x8(a);
+  hi = as_bf16x8(b);
+}
+
+// Branch-free selects on loaded data: a conditional overwrite of a register
+// that a load is filling makes the compiler wait for that load right away, so
+// masking is done with bit operations on the loaded value instead.
+__device__ __forceinline__ unsigned lane_mask(bool c) { return c ? 0xffffffffu : 0u; }
+__device__ __forceinline__ uint4 and4(uint4 a, unsigned m) { return make_uint4(a.x & m, a.y & m, a.z & m, a.w & m); }
+__device__ __forceinline__ uint2 and2(uint2 a, unsigned m) { return make_uint2(a.x & m, a.y & m); }
+__device__ __forceinline__ uint4 sel4(uint4 a, uint4 b, unsigned m) {  // m ? a : b
+  return make_uint4((a.x & m) | (b.x & ~m), (a.y & m) | (b.y & ~m), (a.z & m) | (b.z & ~m), (a.w & m) | (b.w & ~m));
+}
+__device__ __forceinline__ uint2 sel2(uint2 a, uint2 b, unsigned m) {
+  return make_uint2((a.x & m) | (b.x & ~m), (a.y & m) | (b.y & ~m));
+}
+
+template <int D>
+struct DecodeWave {
+  static constexpr int NK = D / 64;
+  bf16x8 qb[NK][2];  // q^T operands
+  f32x4 o[NK][4];    // O^T tiles (hv, jj)
+  float m, l;
+
+  // q: the group's first query head; G heads of D values each, stride D.
+  // Loads are unconditional (lanes past G re-read head G-1) and zeroed after.
+  __device__ __forceinline__ void init(const uint16_t* q, int G) {
+    const int lane = __lane_id();
+    const int hl = lane & 15, gq = lane >> 4;
+    const uint16_t* qh = q + (size_t)min(hl, G - 1) * D;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint4 t = *(const uint4*)(qh + 64 * kk + 16 * gq + 8 * e);
+        qb[kk][e] = as_bf16x8(and4(t, lane_mask(hl < G)));
+      }
+#pragma unroll
+    for (int hv = 0; hv < NK; ++hv)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[hv][jj][r] = 0.f;
+    m = kNegInf;
+    l = 0.f;
+  }
+
+  // Raw register image of one 32-row chunk (K operand rows, V^T source dwords).
+  template <bool INT8>
+  struct Raw {
+    static constexpr int KV = INT8 ? 1 : 2;  // 16-byte loads per (t, kk)
+    uint4 k[2][NK][KV];
+    unsigned v8[NK][8];
+    uint2 v16[NK][8];
+  };
+
+  // One chunk of 32 rows c0 .. c0+31 of `rows` (see the row sources below).
+  // sk multiplies the raw scores (scale * log2 e, times the K scale for INT8),
+  // sv multiplies the chunk's PV partial (the V scale for INT8, else 1).
+  template <bool INT8, class Rows>
+  __device__ __forceinline__ void chunk(const Rows& rows, int c0, float sk, float sv) {
+    Raw<INT8> raw;
+    load<INT8>(rows, c0, raw);
+    compute<INT8>(rows, c0, raw, sk, sv);
+  }
+
+  // Every load is issued unconditionally from an in-range address; absent rows
+  // are zeroed (V) or masked (scores) later with selects, so all of a chunk's
+  // loads can be in flight at once (and the next chunk's during this one).
+  template <bool INT8, class Rows>
+  __device__ __forceinline__ void load(const Rows& rows, int c0, Raw<INT8>& raw) const {
+    const int lane = __lane_id();
+    const int hl = lane & 15, gq = lane >> 4;
+    constexpr int KV = Raw<INT8>::KV;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const char* kp = (const char*)rows.kaddr(c0 + 16 * t + hl);
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+        for (int e = 0; e < KV; ++e)
+          raw.k[t][kk][e] = *(const uint4*)(kp + (INT8 ? 1 : 2) * (64 * kk + 16 * gq + 8 * e));
+    }
+#pragma unroll
+    for (int hv = 0; hv < NK; ++hv)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const char* vp = (const char*)rows.vaddr(c0 + 16 * (j >> 2) + 4 * gq + (j & 3));
+        if (INT8) raw.v8[hv][j] = *(const unsigned*)(vp + 64 * hv + 4 * hl);
+        else raw.v16[hv][j] = *(const uint2*)(vp + 2 * (64 * hv + 4 * hl));
+      }
+  }
+
+  template <bool INT8, class Rows>
+  __device__ __forceinline__ void compute(const Rows& rows, int c0, Raw<INT8>& raw, float sk, float sv) {
+    const int lane = __lane_id();
+    const int hl = lane & 15, gq = lane >> 4;
+    constexpr int KV = Raw<INT8>::KV;
+    auto& kraw = raw.k;
+    auto& vraw8 = raw.v8;
+    auto& vraw16 = raw.v16;
+    if (Rows::kHasAlt) {  // the row being replaced comes from the new token
+      uint4 kalt[NK][KV];
+      uint2 valt[NK];
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+#pragma unroll
+        for (int e = 0; e < KV; ++e) kalt[kk][e] = *(const uint4*)((const uint16_t*)rows.kalt + 64 * kk + 16 * gq + 8 * e);
+        valt[kk] = *(const uint2*)((const uint16_t*)rows.valt + 64 * kk + 4 * hl);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const unsigned am = lane_mask(rows.is_alt(c0 + 16 * t + hl));
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+          for (int e = 0; e < KV; ++e) kraw[t][kk][e] = sel4(kalt[kk][e], kraw[t][kk][e], am);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const unsigned am = lane_mask(rows.is_alt(c0 + 16 * (j >> 2) + 4 * gq + (j & 3)));
+#pragma unroll
+        for (int hv = 0; hv < NK; ++hv) vraw16[hv][j] = sel2(valt[hv], vraw16[hv][j], am);
+      }
+    }
+    if (!Rows::kAllValid) {  // absent rows contribute nothing (their bytes may be anything)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const unsigned ok = lane_mask(rows.valid(c0 + 16 * (j >> 2) + 4 * gq + (j & 3)));
+#pragma unroll
+        for (int hv = 0; hv < NK; ++hv) {
+          if (INT8) vraw8[hv][j] &= ok;
+          else vraw16[hv][j] = and2(vraw16[hv][j], ok);
+        }
+      }
+    }
+    f32x4 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[t][r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        bf16x8 a0, a1;
+        if (INT8) {
+          cvt16(kraw[t][kk][0], a0, a1);
+        } else {
+          a0 = as_bf16x8(kraw[t][kk][0]);
+          a1 = as_bf16x8(kraw[t][kk][KV - 1]);
+        }
+        s[t] = mfma16(a0, qb[kk][0], s[t]);
+        s[t] = mfma16(a1, qb[kk][1], s[t]);
+      }
+    }
+    bf16x8 va[NK][4];
+#pragma unroll
+    for (int hv = 0; hv < NK; ++hv) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        u32x4 t;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (INT8) {
+            t[q] = pack_bf16x2(i8(vraw8[hv][2 * q], jj), i8(vraw8[hv][2 * q + 1], jj));
+          } else {
+            const unsigned x0 = (jj < 2) ? vraw16[hv][2 * q].x : vraw16[hv][2 * q].y;
+            const unsigned x1 = (jj < 2) ? vraw16[hv][2 * q + 1].x : vraw16[hv][2 * q + 1].y;
+            // low or high bf16 of each dword -> one packed pair
+            t[q] = (jj & 1) ? __builtin_amdgcn_perm(x1, x0, 0x07060302u)
+                            : __builtin_amdgcn_perm(x1, x0, 0x05040100u);
+          }
+        }
+        va[hv][jj] = as_bf16x8(t);
+      }
+    }
+    float x[8];
+    float mx = kNegInf;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = s[t][r] * sk;
+        if (!Rows::kAllValid && !rows.valid(c0 + 16 * t + 4 * gq + r)) v = kNegInf;
+        x[4 * t + r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m, mx);
+    const float base = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(m - base);
+    // P is rounded to bf16 for the MFMA; the normaliser sums the same rounded
+    // values, so a row dominated by one key returns that key's value exactly.
+    float ps = 0.f;
+    u32x4 pw;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float p0 = fast_exp2(x[2 * q] - base), p1 = fast_exp2(x[2 * q + 1] - base);
+      pw[q] = pack_bf16x2(p0, p1);
+      ps += bf16lo(pw[q]) + bf16hi(pw[q]);
+    }
+    l = l * alpha + ps;
+    m = m_new;
+    const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+    for (int hv = 0; hv < NK; ++hv)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        f32x4 part = {0.f, 0.f, 0.f, 0.f};
+        part = mfma16(va[hv][jj], pb, part);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[hv][jj][r] = fmaf(o[hv][jj][r], alpha, sv * part[r]);
+      }
+  }
+
+  // Write this wave's state for the heads it serves (lane%16 < G) to LDS:
+  // sm_m/sm_l [waves][16], sm_o [waves][16][D].
+  __device__ __forceinline__ void stash(float (*sm_m)[16], float (*sm_l)[16], float (*sm_o)[16][D],
+                                        int w, int G) {
+    const int lane = __lane_id();
+    const int hl = lane & 15, gq = lane >> 4;
+    float lsum = l;
+    lsum += __shfl_xor(lsum, 16);
+    lsum += xor32(lsum);
+    if (hl < G) {
+#pragma unroll
+      for (int hv = 0; hv < NK; ++hv)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sm_o[w][hl][64 * hv + 16 * gq + 4 * r + jj] = o[hv][jj][r];
+      if (gq == 0) {
+        sm_m[w][hl] = m;
+        sm_l[w][hl] = lsum;
+      }
+    }
+  }
+};
+
+// Merge NW stashed wave states for (head, d): returns acc, sets M and Lsum.
+template <int NW, int D>
+__device__ __forceinline__ float merge_waves(const float (*sm_m)[16], const float (*sm_l)[16],
+                                             const float (*sm_o)[16][D], int head, int d,
+                                             float& M, float& Ls) {
+  M = kNegInf;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) M = fmaxf(M, sm_m[i][head]);
+  float O = 0.f;
+  Ls = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const float f = (sm_m[i][head] == kNegInf) ? 0.f : fast_exp2(sm_m[i][head] - M);
+    O += f * sm_o[i][head][d];
+    Ls += f * sm_l[i][head];
+  }
+  return O;
+}
+
+// ------------------------------------------------------------ row sources ----
+// kaddr/vaddr return an in-range row address for any row of a chunk; valid()
+// says whether the row takes part; is_alt() marks the row whose data comes from
+// kalt/valt instead (a ring slot being overwritten by the new token).
+
+// Contiguous INT8 rows (always in range: callers pass whole 32-row blocks).
+template <int D>
+struct Int8Rows {
+  static constexpr bool kAllValid = true;
+  static constexpr bool kHasAlt = false;
+  const int8_t* k;
+  const int8_t* v;
+  const void* kalt = nullptr;
+  const void* valt = nullptr;
+  __device__ __forceinline__ const void* kaddr(int row) const { return k + (size_t)row * D; }
+  __device__ __forceinline__ const void* vaddr(int row) const { return v + (size_t)row * D; }
+  __device__ __forceinline__ bool valid(int) const { return true; }
+  __device__ __forceinline__ bool is_alt(int) const { return false; }
+};
+
+// Contiguous bf16 rows; rows >= end are absent.
+template <int D>
+struct Bf16Rows {
+  static constexpr bool kAllValid = false;
+  static constexpr bool kHasAlt = false;
+  const uint16_t* k;
+  const uint16_t* v;
+  int end;
+  const void* kalt = nullptr;
+  const void* valt = nullptr;
+  __device__ __forceinline__ const void* kaddr(int row) const { return k + (size_t)min(row, end - 1) * D; }
+  __device__ __forceinline__ const void* vaddr(int row) const { return v + (size_t)min(row, end - 1) * D; }
+  __device__ __forceinline__ bool valid(int row) const { return row < end; }
+  __device__ __forceinline__ bool is_alt(int) const { return false; }
+};
+
+// A W-slot ring after appending position p at slot p mod W.  Slot s holds
+// position p - ((p - s) mod W); it is attended when that position is >= 0.  The
+// new token's K/V comes from kalt/valt (its ring slot is being overwritten).
+template <int D>
+struct RingRows {
+  static constexpr bool kAllValid = false;
+  static constexpr bool kHasAlt = true;
+  const uint16_t* k;
+  const uint16_t* v;
+  const void* kalt;
+  const void* valt;
+  int W, slot, p;
+  __device__ __forceinline__ const void* kaddr(int s) const { return k + (size_t)min(s, W - 1) * D; }
+  __device__ __forceinline__ const void* vaddr(int s) const { return v + (size_t)min(s, W - 1) * D; }
+  __device__ __forceinline__ bool valid(int s) const { return s < W && (slot - s + W) % W <= p; }
+  __device__ __forceinline__ bool is_alt(int s) const { return s == slot; }
+};
+
+}  // namespace hsk
