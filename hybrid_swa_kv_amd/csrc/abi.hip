@@ -66,6 +66,8 @@ int swa_prefill(const void* q, const void* k, const void* v, void* out, int B, i
   if (dtype != HSK_F32 && dtype != HSK_BF16) return HSK_ERR_UNSUPPORTED;
   if (!std::isfinite(scale) || scale <= 0.f) return HSK_ERR_SHAPE;
   if ((long long)L > (1ll << 30) || (long long)B * L * Hq > (1ll << 31) - 1) return HSK_ERR_SHAPE;
+  // K/V tiles are fetched with 32-bit byte offsets from each sequence's start
+  if (dtype == HSK_BF16 && (long long)L * Hkv * D * 2 >= (1ll << 32)) return HSK_ERR_UNSUPPORTED;
   if (ring_k && ring_w <= 0) return HSK_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return HSK_ERR_ALIGN;
   if (ring_k && (!aligned16(ring_k) || !aligned16(ring_v))) return HSK_ERR_ALIGN;
@@ -181,7 +183,7 @@ int blocksparse_select_attend(const void* q, const void* k, const void* v, void*
   if (int rc = check_heads(Hq, Hkv, D)) return rc;
   if (block != 64 || topk > 256) return HSK_ERR_UNSUPPORTED;
   if (L % block != 0) return HSK_ERR_SHAPE;
-  if (L / block > 4096) return HSK_ERR_UNSUPPORTED;
+  if (L / block > 4096 || (long long)L * Hkv * D * 2 >= (1ll << 32)) return HSK_ERR_UNSUPPORTED;
   if (!std::isfinite(scale) || scale <= 0.f) return HSK_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (sel && !aligned4(sel)))
     return HSK_ERR_ALIGN;

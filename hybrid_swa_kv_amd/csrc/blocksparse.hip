@@ -165,8 +165,7 @@ __global__ __launch_bounds__(SEL_THREADS) void bs_select_kernel(BlockSparseArgs 
 template <int D>
 __global__ __launch_bounds__(AT_THREADS) void bs_attend_kernel(BlockSparseArgs a) {
   using C = FtCfg<D>;
-  // one K/V tile buffer (33 KB with the lists): four workgroups fit per CU
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::TILE];
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * C::TILE];
   __shared__ int list[256];                  // selected blocks before the window
   __shared__ unsigned selbits[SEL_MAXNB / 32];
   __shared__ int s_npre;
@@ -214,23 +213,18 @@ __global__ __launch_bounds__(AT_THREADS) void bs_attend_kernel(BlockSparseArgs a
   FlashWave<D> fw;
   fw.init(a.q + ((size_t)row * a.Hq + h) * D);
 
-  const size_t stride = (size_t)a.Hkv * D;
-  const uint16_t* kbase = a.k + (size_t)g * D;
-  const uint16_t* vbase = a.v + (size_t)g * D;
-  TileStage<D, AT_THREADS> stg;
+  TileDma<D, AT_THREADS> dma;
+  dma.init(a.k + (size_t)g * D, a.v + (size_t)g * D, (unsigned)(a.Hkv * D * 2), L, w);
   auto tile_of = [&](int it) { return it < npre ? list[it] : kw0 + (it - npre); };
-  stg.load(kbase, vbase, stride, tile_of(0), L);
-  stg.store(smem);
+  dma.issue(tile_of(0), smem);
   for (int it = 0; it < ntiles; ++it) {
-    __syncthreads();                         // tile it visible
+    wait_vmem();
+    __syncthreads();
     const int kt = tile_of(it);
-    if (it + 1 < ntiles) stg.load(kbase, vbase, stride, tile_of(it + 1), L);
+    if (it + 1 < ntiles) dma.issue(tile_of(it + 1), smem + ((it + 1) & 1) * 2 * C::TILE);
+    const char* ks = smem + (it & 1) * 2 * C::TILE;
     const bool full = (selbits[kt >> 5] >> (kt & 31)) & 1u;
-    fw.tile(smem, smem + C::TILE, kt * FT_BN, r0, row, W, full, a.scale_log2);
-    if (it + 1 < ntiles) {
-      __syncthreads();                       // every wave is done reading tile it
-      stg.store(smem);
-    }
+    fw.tile(ks, ks + C::TILE, kt * FT_BN, r0, row, W, full, a.scale_log2);
   }
   fw.store(a.out + ((size_t)row * a.Hq + h) * D);
 }

@@ -91,6 +91,58 @@ struct TileStage {
   }
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until this wave's vector-memory operations (here: LDS DMA loads) are done.
+__device__ __forceinline__ void wait_vmem() {
+  // s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maximum (no wait)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Global -> LDS staging by buffer_load_dwordx4 ... lds (no registers involved).
+// One instruction moves 1 KB: lane i's 16 bytes land at LDS base + 16 i, so each
+// lane fetches the global chunk that the XOR swizzle places there.  Reads past
+// num_records return zero, which pads the last partial tile.  Offsets are 32-bit
+// byte offsets from a per-(sequence, head) base.
+template <int D, int NT>
+struct TileDma {
+  using C = FtCfg<D>;
+  static constexpr int RPI = 1024 / (D * 2);                 // rows per 1 KB instruction
+  static constexpr int PER_WAVE = FT_BN / RPI / (NT / 64);   // instructions per wave per tensor
+  __amdgpu_buffer_rsrc_t rk, rv;
+  unsigned voff[PER_WAVE];
+  unsigned tile_bytes;  // bytes between consecutive 64-row tiles
+  int wave_lds;         // this wave's first 1 KB block in a tile
+
+  // kbase/vbase: row 0 of this head; row stride in bytes; nrows valid rows
+  __device__ __forceinline__ void init(const uint16_t* kbase, const uint16_t* vbase, unsigned row_bytes,
+                                       int nrows, int wave) {
+    const unsigned nrec = (unsigned)(nrows - 1) * row_bytes + D * 2;
+    rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, (int)nrec, 0x00020000);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, (int)nrec, 0x00020000);
+    tile_bytes = FT_BN * row_bytes;
+    wave_lds = wave * PER_WAVE * 1024;
+    const int lane = __lane_id();
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int blk = wave * PER_WAVE + i;
+      const int row = blk * RPI + lane / C::NCH;
+      const int chunk = (lane % C::NCH) ^ ft_swz<C::NCH>(row);
+      voff[i] = (unsigned)row * row_bytes + chunk * 16;
+    }
+  }
+  // start loading tile kt into the LDS buffer kv_lds (K then V, TILE bytes each)
+  __device__ __forceinline__ void issue(int kt, char* kv_lds) const {
+    const unsigned so = (unsigned)kt * tile_bytes;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kv_lds + wave_lds + i * 1024), 16, voff[i], so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(kv_lds + C::TILE + wave_lds + i * 1024), 16, voff[i],
+                                               so, 0, 0);
+    }
+  }
+};
+
 template <int D>
 struct FlashWave {
   using C = FtCfg<D>;

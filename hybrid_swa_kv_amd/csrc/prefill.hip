@@ -1,7 +1,8 @@
 // Causal sliding-window / full GQA prefill for gfx950.
 //
 // bf16 path: one workgroup = 4 waves = 128 query rows of one head; the key axis
-// is walked in 64-key tiles staged in LDS (double buffered).  Each wave owns 32
+// is walked in 64-key tiles that LDS DMA (buffer_load ... lds) stages into a
+// double buffer one tile ahead.  Each wave owns 32
 // query rows and computes S^T = K * Q^T with v_mfma_f32_32x32x16_bf16, so every
 // lane holds 32 of its row's 64 scores and the other 32 sit in lane ^ 32: the
 // online softmax needs one permlane32 swap per tile.  P stays in registers and
@@ -55,20 +56,19 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(PrefillArgs
   FlashWave<D> fw;
   fw.init(row < L ? a.q + ((size_t)(b * (size_t)L + row) * a.Hq + h) * D : nullptr);
 
-  const size_t stride = (size_t)a.Hkv * D;
   const uint16_t* kbase = a.k + ((size_t)b * L * a.Hkv + g) * D;
   const uint16_t* vbase = a.v + ((size_t)b * L * a.Hkv + g) * D;
-  TileStage<D, PF_THREADS> stg;
-  stg.load(kbase, vbase, stride, kt0, L);
-  stg.store(smem);
+  TileDma<D, PF_THREADS> dma;
+  dma.init(kbase, vbase, (unsigned)(a.Hkv * D * 2), L, w);
+  dma.issue(kt0, smem);
 
   for (int it = 0; it < ntiles; ++it) {
-    __syncthreads();
+    wait_vmem();      // this wave's part of tile it has landed
+    __syncthreads();  // ... everyone's has, and tile it-1's buffer is free
     const int kt = kt0 + it;
-    if (it + 1 < ntiles) stg.load(kbase, vbase, stride, kt + 1, L);
+    if (it + 1 < ntiles) dma.issue(kt + 1, smem + ((it + 1) & 1) * 2 * C::TILE);
     const char* ks = smem + (it & 1) * 2 * C::TILE;
     fw.tile(ks, ks + C::TILE, kt * FT_BN, r0, row, W, false, a.scale_log2);
-    if (it + 1 < ntiles) stg.store(smem + ((it + 1) & 1) * 2 * C::TILE);
   }
   fw.store(row < L ? a.o + ((size_t)(b * (size_t)L + row) * a.Hq + h) * D : nullptr);
 }
