@@ -149,6 +149,12 @@ struct FlashWave {
   bf16x8 qf[C::DC];
   f32x16 o[C::DB];
   float m, l;
+  // Per-lane LDS byte offsets of the K reads (k-step c, key sub-block 0) and the
+  // V^T reads (d block, low/high 8 keys, key group 0).  The swizzle of a lane's
+  // row does not change between key sub-blocks or key groups, so every other
+  // read is one of these plus a constant.
+  int ko[C::DC];
+  int vo[C::DB][2];
 
   // qrow: this lane's query row (D values) or nullptr for rows past the end
   __device__ __forceinline__ void init(const uint16_t* qrow) {
@@ -165,33 +171,51 @@ struct FlashWave {
       for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
     m = kNegInf;
     l = 0.f;
+#pragma unroll
+    for (int c = 0; c < C::DC; ++c) ko[c] = ft_off<C::NCH>(lane & 31, 2 * c + (lane >> 5));
+    const int gq = lane >> 4, sl = lane & 15;
+    const int kr = 4 * (gq >> 1) + (sl >> 2);
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d) {
+      const int col = 32 * d + 16 * (gq & 1) + 4 * (sl & 3);
+      vo[d][0] = ft_off<C::NCH>(kr, col >> 3) + ((col & 7) << 1);
+      vo[d][1] = ft_off<C::NCH>(kr + 8, col >> 3) + ((col & 7) << 1);
+    }
   }
 
-  // One 64-key tile at key position k0 held in LDS (K at ks, V at vs).
-  // r0: first query row of the wave; row: this lane's row; visibility is
-  // 0 <= row - key < W unless `full` (every key of the tile visible to every row).
-  __device__ __forceinline__ void tile(const char* ks, const char* vs, int k0, int r0, int row,
-                                       int W, bool full, float scale_log2) {
-    const int lane = __lane_id();
-    bool need_mask = false;
-    if (!full) {
-      if ((k0 > r0 + 31) || (k0 + FT_BN - 1 < r0 - W + 1)) return;  // nothing visible
-      need_mask = !((k0 + FT_BN - 1 <= r0) && (r0 + 31 - k0 < W));
-    }
-    f32x16 s[2];
+  // Visibility of the 64-key tile at k0 for rows r0 .. r0+31 (0 <= row - key < W,
+  // or every key when `full`): 0 none, 1 partly (edge tile, needs the mask), 2 all.
+  __device__ __forceinline__ static int visible(int k0, int r0, int W, bool full) {
+    if (full) return 2;
+    if ((k0 > r0 + 31) || (k0 + FT_BN - 1 < r0 - W + 1)) return 0;
+    return ((k0 + FT_BN - 1 <= r0) && (r0 + 31 - k0 < W)) ? 2 : 1;
+  }
+
+  // S^T for the tile whose K rows are at ks: lane l gets the scores of query row
+  // l%32 with keys 32 sub + 8 (r/4) + 4 (l/32) + r%4 in s[sub][r].
+  __device__ __forceinline__ void qk(const char* ks, f32x16 (&s)[2]) const {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[sub][r] = 0.f;
-      const int key = 32 * sub + (lane & 31);
+    // the two key blocks are independent accumulation chains: alternate them
 #pragma unroll
-      for (int c = 0; c < C::DC; ++c) {
-        const int ch = 2 * c + (lane >> 5);
-        const bf16x8 ka = *(const bf16x8*)(ks + ft_off<C::NCH>(key, ch));
+    for (int c = 0; c < C::DC; ++c)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        // key 32 sub + lane%32, chunk 2c + lane/32
+        const bf16x8 ka = *(const bf16x8*)(ks + 32 * sub * C::NCH * 16 + ko[c]);
         s[sub] = mfma32(ka, qf[c], s[sub]);
       }
-    }
-    if (__builtin_expect(need_mask, 0)) {  // edge tile (wave-uniform branch)
+  }
+
+  // Online softmax of one tile's scores (masked when `mask`; k0: first key of the
+  // tile, row: this lane's query row): updates m, l (and rescales o) and packs the
+  // probabilities as bf16 pairs in the key order the P^T operand of pv() expects.
+  __device__ __forceinline__ void softmax(f32x16 (&s)[2], bool mask, int k0, int row, int W,
+                                          float scale_log2, u32x4 (&pw)[4]) {
+    const int lane = __lane_id();
+    if (__builtin_expect(mask, 0)) {  // edge tile (wave-uniform branch)
       // key of register r: k0 + 32 sub + 8 (r/4) + 4 (lane/32) + r%4
       const int d0 = row - k0 - 4 * (lane >> 5);
 #pragma unroll
@@ -224,7 +248,6 @@ struct FlashWave {
     }
     const float negm = (m == kNegInf) ? 0.f : -m;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    u32x4 pw[4];
 #pragma unroll
     for (int kap = 0; kap < 4; ++kap) {
       const int sub = kap >> 1, half = kap & 1;
@@ -242,25 +265,40 @@ struct FlashWave {
         l = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l, false);
       }
     }
+  }
 
-    const int gq = lane >> 4, sl = lane & 15;
+  // O^T += V^T * P^T for the tile whose V rows are at vs.
+  __device__ __forceinline__ void pv(const char* vs, const u32x4 (&pw)[4]) {
 #pragma unroll
     for (int kap = 0; kap < 4; ++kap) {
       const bf16x8 pb = as_bf16x8(pw[kap]);
-      // k-slot j of lane group gq/2 <-> key 16 kap + 4 (gq/2) + j (j < 4) or + 8 + (j - 4)
-      const int kr = 16 * kap + 4 * (gq >> 1) + (sl >> 2);
+      // k-slot j of lane group gq/2 <-> key 16 kap + 4 (gq/2) + j (j < 4) or + 8 + (j - 4);
+      // lane (gq, sl) reads V row 16 kap + 4 (gq/2) + sl/4 (+ 8), columns
+      // 32 d + 16 (gq&1) + 4 (sl&3) .. + 3
+      const char* vk = vs + 16 * kap * C::NCH * 16;
 #pragma unroll
       for (int d = 0; d < C::DB; ++d) {
-        const int col = 32 * d + 16 * (gq & 1) + 4 * (sl & 3);
-        const int o0 = ft_off<C::NCH>(kr, col >> 3) + ((col & 7) << 1);
-        const int o1 = ft_off<C::NCH>(kr + 8, col >> 3) + ((col & 7) << 1);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + o0));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + o1));
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vk + vo[d][0]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vk + vo[d][1]));
         typedef __attribute__((ext_vector_type(8))) short s16x8;
         const s16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         o[d] = mfma32(__builtin_bit_cast(bf16x8, va), pb, o[d]);
       }
     }
+  }
+
+  // One 64-key tile at key position k0 held in LDS (K at ks, V at vs).
+  // r0: first query row of the wave; row: this lane's row; visibility is
+  // 0 <= row - key < W unless `full` (every key of the tile visible to every row).
+  __device__ __forceinline__ void tile(const char* ks, const char* vs, int k0, int r0, int row,
+                                       int W, bool full, float scale_log2) {
+    const int v = visible(k0, r0, W, full);
+    if (v == 0) return;
+    f32x16 s[2];
+    u32x4 pw[4];
+    qk(ks, s);
+    softmax(s, v == 1, k0, row, W, scale_log2, pw);
+    pv(vs, pw);
   }
 
   // normalise and store this lane's row (orow = nullptr: row not stored)

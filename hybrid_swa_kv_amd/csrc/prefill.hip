@@ -62,14 +62,20 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(PrefillArgs
   dma.init(kbase, vbase, (unsigned)(a.Hkv * D * 2), L, w);
   dma.issue(kt0, smem);
 
-  for (int it = 0; it < ntiles; ++it) {
+  // unrolled by two so each buffer's LDS offsets are compile-time constants
+  auto step = [&](int it, char* cur, char* nxt) {
     wait_vmem();      // this wave's part of tile it has landed
     __syncthreads();  // ... everyone's has, and tile it-1's buffer is free
     const int kt = kt0 + it;
-    if (it + 1 < ntiles) dma.issue(kt + 1, smem + ((it + 1) & 1) * 2 * C::TILE);
-    const char* ks = smem + (it & 1) * 2 * C::TILE;
-    fw.tile(ks, ks + C::TILE, kt * FT_BN, r0, row, W, false, a.scale_log2);
+    if (it + 1 < ntiles) dma.issue(kt + 1, nxt);
+    fw.tile(cur, cur + C::TILE, kt * FT_BN, r0, row, W, false, a.scale_log2);
+  };
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    step(it, smem, smem + 2 * C::TILE);
+    step(it + 1, smem + 2 * C::TILE, smem);
   }
+  if (it < ntiles) step(it, smem, smem + 2 * C::TILE);
   fw.store(row < L ? a.o + ((size_t)(b * (size_t)L + row) * a.Hq + h) * D : nullptr);
 }
 
