@@ -64,6 +64,15 @@ __device__ __forceinline__ float xor32(float x) {
   return __uint_as_float((__lane_id() & 32) ? r[0] : r[1]);
 }
 
+// value held by lane l ^ 16 (v_permlane16_swap: rows of 16 lanes trade places
+// pairwise; no LDS round trip, unlike a bpermute)
+__device__ __forceinline__ float xor16(float x) {
+  unsigned u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  // lanes in even rows receive the next row's value in r[1]; odd rows in r[0]
+  return __uint_as_float((__lane_id() & 16) ? r[0] : r[1]);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));

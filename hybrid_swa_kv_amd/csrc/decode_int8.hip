@@ -26,7 +26,7 @@ constexpr int DQ_THREADS = 256;
 template <int D>
 __global__ __launch_bounds__(DQ_THREADS) void int8_decode_kernel(Int8DecodeArgs a) {
   __shared__ float sm_m[4][16], sm_l[4][16];
-  __shared__ float sm_o[4][16][D];
+  __shared__ float sm_o[4][16][D + 1];
 
   const int nsplit = a.ns8 + a.nsh;
   const int split = blockIdx.x % nsplit;

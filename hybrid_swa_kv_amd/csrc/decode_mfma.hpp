@@ -1,9 +1,9 @@
 // One-token decode on v_mfma_f32_16x16x32_bf16, shared by the ring decode and
 // the INT8 + bf16 decode.
 //
-// A wave processes 32-key chunks with the (up to 16) query heads of one KV head
-// on the MFMA N axis; lane l serves head l%16 (zero query for unused heads) and
-// lane group g = l/16:
+// A wave processes 32-key (or 16-key) chunks with the (up to 16) query heads of
+// one KV head on the MFMA N axis; lane l serves head l%16 (lanes past the group
+// duplicate its last head) and lane group g = l/16:
 //   S   = K * q^T      A = K rows (16 keys x 32 d), B = q^T
 //                      -> lane l holds the scores of keys 16t + 4g + r (t<2, r<4)
 //   O^T += V^T * P^T   A = V^T (16 d x 32 keys), B = P^T: a lane's 8 probabilities
@@ -52,15 +52,26 @@ __device__ __forceinline__ uint2 sel2(uint2 a, uint2 b, unsigned m) {
   return make_uint2((a.x & m) | (b.x & ~m), (a.y & m) | (b.y & ~m));
 }
 
-template <int D>
+// BLOCKED selects which 8 d values lane group g contributes to QK MFMA (kk, e):
+//   false: d = 64 kk + 16 g + 8 e + j (a 16-byte load of 16 INT8 codes feeds e = 0, 1)
+//   true:  d = 64 kk + 32 e + 8 g + j (bf16 rows: each load instruction then reads
+//          64 contiguous bytes of a row instead of 16 bytes every 32)
+// Any consistent assignment of d to the contraction slots gives the same scores.
+template <int D, bool BLOCKED = false>
 struct DecodeWave {
   static constexpr int NK = D / 64;
+  __device__ __forceinline__ static int qk_col(int kk, int e, int gq) {
+    return BLOCKED ? 64 * kk + 32 * e + 8 * gq : 64 * kk + 16 * gq + 8 * e;
+  }
   bf16x8 qb[NK][2];  // q^T operands
   f32x4 o[NK][4];    // O^T tiles (hv, jj)
   float m, l;
 
   // q: the group's first query head; G heads of D values each, stride D.
-  // Loads are unconditional (lanes past G re-read head G-1) and zeroed after.
+  // Lanes past G re-read head G-1: every head is its own MFMA column, so those
+  // duplicate columns never mix with the real ones and are simply not stored.
+  // (No use of the loaded values here: the ring/cache loads that follow are
+  // issued before anything waits for q.)
   __device__ __forceinline__ void init(const uint16_t* q, int G) {
     const int lane = __lane_id();
     const int hl = lane & 15, gq = lane >> 4;
@@ -69,8 +80,7 @@ struct DecodeWave {
     for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const uint4 t = *(const uint4*)(qh + 64 * kk + 16 * gq + 8 * e);
-        qb[kk][e] = as_bf16x8(and4(t, lane_mask(hl < G)));
+        qb[kk][e] = as_bf16x8(*(const uint4*)(qh + qk_col(kk, e, gq)));
       }
 #pragma unroll
     for (int hv = 0; hv < NK; ++hv)
@@ -91,78 +101,102 @@ struct DecodeWave {
     uint2 v16[NK][8];
   };
 
-  // One chunk of 32 rows c0 .. c0+31 of `rows` (see the row sources below).
-  // sk multiplies the raw scores (scale * log2 e, times the K scale for INT8),
-  // sv multiplies the chunk's PV partial (the V scale for INT8, else 1).
-  template <bool INT8, class Rows>
+  // The replacing row of a ring (bf16 K operand chunks and V^T source dwords),
+  // loaded once per workgroup instead of once per chunk.
+  struct AltRow {
+    uint4 k[NK][2];
+    uint2 v[NK];
+  };
+  template <class Rows>
+  __device__ __forceinline__ void load_alt(const Rows& rows, AltRow& alt) const {
+    const int lane = __lane_id();
+    const int hl = lane & 15, gq = lane >> 4;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        alt.k[kk][e] = *(const uint4*)((const uint16_t*)rows.kalt + qk_col(kk, e, gq));
+      alt.v[kk] = *(const uint2*)((const uint16_t*)rows.valt + 64 * kk + 4 * hl);
+    }
+  }
+
+  // One chunk of 16 NT rows c0 .. c0+16 NT-1 of `rows` (NT = 1 or 2 blocks of 16
+  // keys; see the row sources below).  sk multiplies the raw scores (scale *
+  // log2 e, times the K scale for INT8), sv multiplies the chunk's PV partial
+  // (the V scale for INT8, else 1).
+  template <bool INT8, int NT = 2, class Rows>
   __device__ __forceinline__ void chunk(const Rows& rows, int c0, float sk, float sv) {
     Raw<INT8> raw;
-    load<INT8>(rows, c0, raw);
-    compute<INT8>(rows, c0, raw, sk, sv);
+    load<INT8, NT>(rows, c0, raw);
+    compute<INT8, NT>(rows, c0, raw, sk, sv);
   }
 
   // Every load is issued unconditionally from an in-range address; absent rows
   // are zeroed (V) or masked (scores) later with selects, so all of a chunk's
   // loads can be in flight at once (and the next chunk's during this one).
-  template <bool INT8, class Rows>
+  template <bool INT8, int NT = 2, class Rows>
   __device__ __forceinline__ void load(const Rows& rows, int c0, Raw<INT8>& raw) const {
+    static_assert(!(INT8 && BLOCKED), "INT8 rows use the interleaved operand layout");
     const int lane = __lane_id();
     const int hl = lane & 15, gq = lane >> 4;
     constexpr int KV = Raw<INT8>::KV;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const char* kp = (const char*)rows.kaddr(c0 + 16 * t + hl);
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
         for (int e = 0; e < KV; ++e)
-          raw.k[t][kk][e] = *(const uint4*)(kp + (INT8 ? 1 : 2) * (64 * kk + 16 * gq + 8 * e));
+          raw.k[t][kk][e] = *(const uint4*)(kp + (INT8 ? 64 * kk + 16 * gq : 2 * qk_col(kk, e, gq)));
     }
 #pragma unroll
     for (int hv = 0; hv < NK; ++hv)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4 * NT; ++j) {
         const char* vp = (const char*)rows.vaddr(c0 + 16 * (j >> 2) + 4 * gq + (j & 3));
         if (INT8) raw.v8[hv][j] = *(const unsigned*)(vp + 64 * hv + 4 * hl);
         else raw.v16[hv][j] = *(const uint2*)(vp + 2 * (64 * hv + 4 * hl));
       }
   }
 
-  template <bool INT8, class Rows>
+  template <bool INT8, int NT = 2, class Rows>
   __device__ __forceinline__ void compute(const Rows& rows, int c0, Raw<INT8>& raw, float sk, float sv) {
+    AltRow none;
+    compute<INT8, NT>(rows, c0, raw, sk, sv, none);
+  }
+
+  // alt: the replacing row (used when Rows::kHasAlt and it falls in this chunk)
+  template <bool INT8, int NT = 2, class Rows>
+  __device__ __forceinline__ void compute(const Rows& rows, int c0, Raw<INT8>& raw, float sk, float sv,
+                                          const AltRow& alt) {
     const int lane = __lane_id();
     const int hl = lane & 15, gq = lane >> 4;
     constexpr int KV = Raw<INT8>::KV;
     auto& kraw = raw.k;
     auto& vraw8 = raw.v8;
     auto& vraw16 = raw.v16;
-    if (Rows::kHasAlt) {  // the row being replaced comes from the new token
-      uint4 kalt[NK][KV];
-      uint2 valt[NK];
+    // Both conditions are wave-uniform: chunks without the replaced row, and
+    // chunks whose rows are all present, skip the per-register selects.
+    if (Rows::kHasAlt && !INT8 && rows.alt_in(c0, 16 * NT)) {
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-#pragma unroll
-        for (int e = 0; e < KV; ++e) kalt[kk][e] = *(const uint4*)((const uint16_t*)rows.kalt + 64 * kk + 16 * gq + 8 * e);
-        valt[kk] = *(const uint2*)((const uint16_t*)rows.valt + 64 * kk + 4 * hl);
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < NT; ++t) {
         const unsigned am = lane_mask(rows.is_alt(c0 + 16 * t + hl));
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
-          for (int e = 0; e < KV; ++e) kraw[t][kk][e] = sel4(kalt[kk][e], kraw[t][kk][e], am);
+          for (int e = 0; e < KV; ++e) kraw[t][kk][e] = sel4(alt.k[kk][e], kraw[t][kk][e], am);
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4 * NT; ++j) {
         const unsigned am = lane_mask(rows.is_alt(c0 + 16 * (j >> 2) + 4 * gq + (j & 3)));
 #pragma unroll
-        for (int hv = 0; hv < NK; ++hv) vraw16[hv][j] = sel2(valt[hv], vraw16[hv][j], am);
+        for (int hv = 0; hv < NK; ++hv) vraw16[hv][j] = sel2(alt.v[hv], vraw16[hv][j], am);
       }
     }
-    if (!Rows::kAllValid) {  // absent rows contribute nothing (their bytes may be anything)
+    const bool partial = !Rows::kAllValid && !rows.all_valid(c0, 16 * NT);
+    if (partial) {  // absent rows contribute nothing (their bytes may be anything)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4 * NT; ++j) {
         const unsigned ok = lane_mask(rows.valid(c0 + 16 * (j >> 2) + 4 * gq + (j & 3)));
 #pragma unroll
         for (int hv = 0; hv < NK; ++hv) {
@@ -172,21 +206,41 @@ struct DecodeWave {
       }
     }
     f32x4 s[2];
+    if (NT == 1) {  // one key block: split its contraction into two chains
+      f32x4 s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[t][r] = 0.f;
+      for (int r = 0; r < 4; ++r) s[0][r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         bf16x8 a0, a1;
         if (INT8) {
-          cvt16(kraw[t][kk][0], a0, a1);
+          cvt16(kraw[0][kk][0], a0, a1);
         } else {
-          a0 = as_bf16x8(kraw[t][kk][0]);
-          a1 = as_bf16x8(kraw[t][kk][KV - 1]);
+          a0 = as_bf16x8(kraw[0][kk][0]);
+          a1 = as_bf16x8(kraw[0][kk][KV - 1]);
         }
-        s[t] = mfma16(a0, qb[kk][0], s[t]);
-        s[t] = mfma16(a1, qb[kk][1], s[t]);
+        s[0] = mfma16(a0, qb[kk][0], s[0]);
+        s1 = mfma16(a1, qb[kk][1], s1);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[0][r] += s1[r];
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[t][r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          bf16x8 a0, a1;
+          if (INT8) {
+            cvt16(kraw[t][kk][0], a0, a1);
+          } else {
+            a0 = as_bf16x8(kraw[t][kk][0]);
+            a1 = as_bf16x8(kraw[t][kk][KV - 1]);
+          }
+          s[t] = mfma16(a0, qb[kk][0], s[t]);
+          s[t] = mfma16(a1, qb[kk][1], s[t]);
+        }
       }
     }
     bf16x8 va[NK][4];
@@ -197,7 +251,9 @@ struct DecodeWave {
         u32x4 t;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          if (INT8) {
+          if (2 * q >= 4 * NT) {  // key slots past the chunk: zero
+            t[q] = 0u;
+          } else if (INT8) {
             t[q] = pack_bf16x2(i8(vraw8[hv][2 * q], jj), i8(vraw8[hv][2 * q + 1], jj));
           } else {
             const unsigned x0 = (jj < 2) ? vraw16[hv][2 * q].x : vraw16[hv][2 * q].y;
@@ -216,12 +272,15 @@ struct DecodeWave {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float v = s[t][r] * sk;
-        if (!Rows::kAllValid && !rows.valid(c0 + 16 * t + 4 * gq + r)) v = kNegInf;
+        float v = kNegInf;
+        if (t < NT) {
+          v = s[t][r] * sk;
+          if (partial && !rows.valid(c0 + 16 * t + 4 * gq + r)) v = kNegInf;
+        }
         x[4 * t + r] = v;
         mx = fmaxf(mx, v);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, xor16(mx));
     mx = fmaxf(mx, xor32(mx));
     const float m_new = fmaxf(m, mx);
     const float base = (m_new == kNegInf) ? 0.f : m_new;
@@ -232,6 +291,10 @@ struct DecodeWave {
     u32x4 pw;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+      if (2 * q >= 4 * NT) {
+        pw[q] = 0u;
+        continue;
+      }
       const float p0 = fast_exp2(x[2 * q] - base), p1 = fast_exp2(x[2 * q + 1] - base);
       pw[q] = pack_bf16x2(p0, p1);
       ps += bf16lo(pw[q]) + bf16hi(pw[q]);
@@ -251,13 +314,14 @@ struct DecodeWave {
   }
 
   // Write this wave's state for the heads it serves (lane%16 < G) to LDS:
-  // sm_m/sm_l [waves][16], sm_o [waves][16][D].
-  __device__ __forceinline__ void stash(float (*sm_m)[16], float (*sm_l)[16], float (*sm_o)[16][D],
+  // sm_m/sm_l [waves][16], sm_o [waves][16][D + 1] (rows padded by one float so
+  // the 16 heads written by one instruction fall in different banks).
+  __device__ __forceinline__ void stash(float (*sm_m)[16], float (*sm_l)[16], float (*sm_o)[16][D + 1],
                                         int w, int G) {
     const int lane = __lane_id();
     const int hl = lane & 15, gq = lane >> 4;
     float lsum = l;
-    lsum += __shfl_xor(lsum, 16);
+    lsum += xor16(lsum);
     lsum += xor32(lsum);
     if (hl < G) {
 #pragma unroll
@@ -277,7 +341,7 @@ struct DecodeWave {
 // Merge NW stashed wave states for (head, d): returns acc, sets M and Lsum.
 template <int NW, int D>
 __device__ __forceinline__ float merge_waves(const float (*sm_m)[16], const float (*sm_l)[16],
-                                             const float (*sm_o)[16][D], int head, int d,
+                                             const float (*sm_o)[16][D + 1], int head, int d,
                                              float& M, float& Ls) {
   M = kNegInf;
 #pragma unroll
@@ -310,7 +374,9 @@ struct Int8Rows {
   __device__ __forceinline__ const void* kaddr(int row) const { return k + (size_t)row * D; }
   __device__ __forceinline__ const void* vaddr(int row) const { return v + (size_t)row * D; }
   __device__ __forceinline__ bool valid(int) const { return true; }
+  __device__ __forceinline__ bool all_valid(int, int) const { return true; }
   __device__ __forceinline__ bool is_alt(int) const { return false; }
+  __device__ __forceinline__ bool alt_in(int, int) const { return false; }
 };
 
 // Contiguous bf16 rows; rows >= end are absent.
@@ -326,7 +392,9 @@ struct Bf16Rows {
   __device__ __forceinline__ const void* kaddr(int row) const { return k + (size_t)min(row, end - 1) * D; }
   __device__ __forceinline__ const void* vaddr(int row) const { return v + (size_t)min(row, end - 1) * D; }
   __device__ __forceinline__ bool valid(int row) const { return row < end; }
+  __device__ __forceinline__ bool all_valid(int r0, int n) const { return r0 + n <= end; }
   __device__ __forceinline__ bool is_alt(int) const { return false; }
+  __device__ __forceinline__ bool alt_in(int, int) const { return false; }
 };
 
 // A W-slot ring after appending position p at slot p mod W.  Slot s holds
@@ -343,8 +411,15 @@ struct RingRows {
   int W, slot, p;
   __device__ __forceinline__ const void* kaddr(int s) const { return k + (size_t)min(s, W - 1) * D; }
   __device__ __forceinline__ const void* vaddr(int s) const { return v + (size_t)min(s, W - 1) * D; }
-  __device__ __forceinline__ bool valid(int s) const { return s < W && (slot - s + W) % W <= p; }
+  __device__ __forceinline__ bool valid(int s) const {
+    // (slot - s) mod W for 0 <= s < W, without a division or a branch
+    const int d = slot - s;
+    return (s < W) & ((d < 0 ? d + W : d) <= p);
+  }
+  // every slot holds a position >= 0 once p >= W - 1
+  __device__ __forceinline__ bool all_valid(int s0, int n) const { return p >= W - 1 && s0 + n <= W; }
   __device__ __forceinline__ bool is_alt(int s) const { return s == slot; }
+  __device__ __forceinline__ bool alt_in(int s0, int n) const { return slot >= s0 && slot < s0 + n; }
 };
 
 }  // namespace hsk

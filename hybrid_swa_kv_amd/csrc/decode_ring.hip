@@ -1,13 +1,16 @@
 // One-token decode against a sliding-window ring buffer (bandwidth bound).
 //
-// One workgroup per (sequence, KV head, group of up to 16 query heads); its 4
-// waves take interleaved 32-slot chunks of the ring and run the 16x16x32 MFMA
+// One workgroup per (sequence, KV head, group of up to 16 query heads); its 8
+// waves take interleaved 16-slot chunks of the ring and run the 16x16x32 MFMA
 // decode of decode_mfma.hpp (heads on the MFMA N axis), then merge their
-// (max, sum, acc) states through LDS behind a single barrier.  Every load of the
-// ring is issued at the start of a chunk, so one HBM round trip covers the
-// 128-slot window.  The new token's K/V is written to slot pos mod W and used
-// from k_new/v_new (the stale slot is never read); slots whose position would be
-// negative (ring not yet full) are neither read nor attended.
+// (max, sum, acc) states through LDS behind a single barrier.  Every load of a
+// chunk (ring rows, the new token, q) is issued before anything waits on one,
+// so one HBM round trip covers a 128-slot window; longer windows keep the next
+// chunk in flight while the current one is computed.  Small chunks keep each
+// wave's serial work short: the decode of one chunk is the kernel's tail once
+// its data has arrived.  The new token's K/V is written to slot pos mod W and
+// used from k_new/v_new (the stale slot is never read); slots whose position
+// would be negative (ring not yet full) are neither read nor attended.
 #include "common.hpp"
 #include "decode_mfma.hpp"
 #include "kernels.hpp"
@@ -16,12 +19,15 @@ namespace hsk {
 
 namespace {
 
-constexpr int RD_THREADS = 256;
+constexpr int RD_WAVES = 8;
+constexpr int RD_THREADS = 64 * RD_WAVES;
+constexpr int RD_CHUNK = 16;                     // slots per wave per step
+constexpr int RD_STRIDE = RD_CHUNK * RD_WAVES;   // slots per workgroup step
 
 template <int D>
 __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs a) {
-  __shared__ float sm_m[4][16], sm_l[4][16];
-  __shared__ float sm_o[4][16][D];
+  __shared__ float sm_m[RD_WAVES][16], sm_l[RD_WAVES][16];
+  __shared__ float sm_o[RD_WAVES][16][D + 1];
 
   const int G = a.Hq / a.Hkv;
   const int HG = G < 16 ? G : 16;  // heads served by this workgroup
@@ -37,32 +43,55 @@ __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs 
   // only the masks do, so the pos load and the ring loads travel together.  A
   // negative pos (a violated precondition) attends nothing, writes no slot and
   // yields zeros.
-  const int p = a.pos[b];
-  const bool ok = p >= 0;
-  const int slot = ok ? p % W : 0;
   const size_t kvoff = (size_t)b * a.Hkv + g;
   uint16_t* rk = a.ring_k + kvoff * (size_t)W * D;
   uint16_t* rv = a.ring_v + kvoff * (size_t)W * D;
   const uint16_t* kn = a.k_new + kvoff * D;
   const uint16_t* vn = a.v_new + kvoff * D;
-  DecodeWave<D> st;
+  DecodeWave<D, true> st;
   st.init(a.q + ((size_t)b * a.Hq + h0) * D, HG);
-  const RingRows<D> rows{rk, rv, kn, vn, W, slot, ok ? p : -1};
-  for (int c0 = 32 * w; c0 < W; c0 += 128) st.template chunk<false>(rows, c0, a.scale_log2, 1.f);
+  // slot and position are only needed for the masks: filled in after the loads
+  RingRows<D> rows{rk, rv, kn, vn, W, 0, -1};
+  typename DecodeWave<D, true>::AltRow alt;
+  st.load_alt(rows, alt);
+  // the new token's rows for the append after the barrier, fetched now (every
+  // thread loads a 16-byte piece; threads t < D/8 store theirs)
+  const int tp = t % (D / 8);
+  const uint4 kn_piece = *(const uint4*)(kn + 8 * tp);
+  const uint4 vn_piece = *(const uint4*)(vn + 8 * tp);
+  // software pipelined over the wave's chunks: chunk c+1 is in flight while c is computed
+  using Raw = typename DecodeWave<D, true>::template Raw<false>;
+  Raw cur, nxt;
+  const int first = RD_CHUNK * w;
+  st.template load<false, 1>(rows, first, cur);
+  __builtin_amdgcn_sched_barrier(0);  // keep the pos load and its use behind the chunk loads
+  const int p = a.pos[b];
+  const bool ok = p >= 0;
+  const int slot = (int)((unsigned)max(p, 0) % (unsigned)W);  // branch-free
+  rows.slot = slot;
+  rows.p = ok ? p : -1;
+  int c0 = first;
+  for (; c0 + RD_STRIDE < W; c0 += 2 * RD_STRIDE) {
+    st.template load<false, 1>(rows, c0 + RD_STRIDE, nxt);
+    st.template compute<false, 1>(rows, c0, cur, a.scale_log2, 1.f, alt);
+    if (c0 + 2 * RD_STRIDE < W) st.template load<false, 1>(rows, c0 + 2 * RD_STRIDE, cur);
+    st.template compute<false, 1>(rows, c0 + RD_STRIDE, nxt, a.scale_log2, 1.f, alt);
+  }
+  if (c0 < W) st.template compute<false, 1>(rows, c0, cur, a.scale_log2, 1.f, alt);
 
   st.stash(sm_m, sm_l, sm_o, w, HG);
   __syncthreads();
   // append (after every read of the ring in this workgroup): the first head
   // group's workgroup writes the new token into its slot
   if (ok && hg == 0 && t < D / 8) {
-    *(uint4*)(rk + (size_t)slot * D + 8 * t) = *(const uint4*)(kn + 8 * t);
-    *(uint4*)(rv + (size_t)slot * D + 8 * t) = *(const uint4*)(vn + 8 * t);
+    *(uint4*)(rk + (size_t)slot * D + 8 * t) = kn_piece;
+    *(uint4*)(rv + (size_t)slot * D + 8 * t) = vn_piece;
   }
   if (ok && hg == 0 && g == 0 && t == 0 && a.slot_out) a.slot_out[b] = slot;
   for (int e = t; e < HG * D; e += RD_THREADS) {
     const int head = e / D, d = e % D;
     float M, Ls;
-    const float O = merge_waves<4, D>(sm_m, sm_l, sm_o, head, d, M, Ls);
+    const float O = merge_waves<RD_WAVES, D>(sm_m, sm_l, sm_o, head, d, M, Ls);
     a.out[((size_t)b * a.Hq + h0 + head) * D + d] = f32_to_bf16(ok ? O / Ls : 0.f);
   }
 }
