@@ -44,6 +44,38 @@ INT8 = dict(B=16, Hq=32, Hkv=8, D=128, ctx=65536, hot=2048)
 SPARSE = dict(L=131072, Hq=32, Hkv=8, D=128, block=64, topk=64, W=1024)
 
 
+# HBM traffic of the headline kernel, from the two rocprofv3 --pmc passes recorded
+# in this file; it is reported only while the kernel's sources hash to the value
+# recorded there (a changed kernel reports null until it is measured again).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ring_decode_kernel_b32_w128_hbm_traffic.txt")
+RING_SOURCES = ("decode_ring.hip", "decode_mfma.hpp", "common.hpp", "kernels.hpp")
+
+
+def ring_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in RING_SOURCES:
+        with open(os.path.join(ROOT, "hybrid_swa_kv_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Bytes per launch recorded for the current ring kernel sources, else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith((" ", "#")))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_sha256") != ring_source_hash():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def pairs_prefill(L: int, W: int) -> int:
     if W <= 0 or W >= L:
         return L * (L + 1) // 2
@@ -156,6 +188,9 @@ def main() -> int:
     ap.add_argument("--rows", default="ring,swa,full,quant,int8,sparse")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 1 GiB device-to-device copy (the reference kernel for "
+                         "scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); the path has no "
@@ -251,6 +286,14 @@ def main() -> int:
                           dtype=torch.uint8, device=dev)
         work["sparse"] = lambda: hsk.blocksparse_select_attend(sq, sk, sv, c["block"], c["topk"], c["W"],
                                                                out=sout, sel=ssel, workspace=sws)
+    if args.calib_copy:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print("[bench] calibration copy of 1 GiB done", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     print("[bench] inputs resident; warming up", file=sys.stderr, flush=True)
 
@@ -339,7 +382,7 @@ def main() -> int:
     if "ring" in res:
         line["roofline"] = {"kernel": "ring_decode_kernel", "bound": "hbm",
                             "achieved": res["ring"]["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                            "frac": res["ring"]["frac_hbm_peak"], "traffic": None}
+                            "frac": res["ring"]["frac_hbm_peak"], "traffic": recorded_traffic()}
     line["rows"] = res
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
