@@ -148,6 +148,7 @@ int attn_decode_int8kv(const void* q, const int8_t* k_codes, const float* k_scal
   if (B <= 0 || T8 < 0 || T8 % 32 != 0 || Th <= 0) return HSK_ERR_SHAPE;
   if (int rc = check_heads(Hq, Hkv, D)) return rc;
   if (Hq / Hkv > 16) return HSK_ERR_UNSUPPORTED;
+  if ((long long)T8 * D >= (1ll << 31)) return HSK_ERR_UNSUPPORTED;  // 32-bit code offsets per head
   if (!std::isfinite(scale)) return HSK_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_hot) || !aligned16(v_hot) || !aligned16(out)) return HSK_ERR_ALIGN;
   if (T8 > 0 && (!aligned16(k_codes) || !aligned16(v_codes) || !aligned4(k_scales) || !aligned4(v_scales)))

@@ -29,8 +29,12 @@ __global__ __launch_bounds__(DQ_THREADS) void int8_decode_kernel(Int8DecodeArgs 
   __shared__ float sm_o[4][16][D + 1];
 
   const int nsplit = a.ns8 + a.nsh;
-  const int split = blockIdx.x % nsplit;
-  const int unit = blockIdx.x / nsplit;  // b * Hkv + g
+  // the bf16 tail splits (twice the bytes of an INT8 split) are dispatched first
+  // so none of them starts in the last round of workgroups
+  const int nhot = a.B * a.Hkv * a.nsh;
+  const int i = blockIdx.x;
+  const int unit = i < nhot ? i / a.nsh : (i - nhot) / a.ns8;  // b * Hkv + g
+  const int split = i < nhot ? a.ns8 + i % a.nsh : (i - nhot) % a.ns8;
   const int g = unit % a.Hkv, b = unit / a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -41,19 +45,34 @@ __global__ __launch_bounds__(DQ_THREADS) void int8_decode_kernel(Int8DecodeArgs 
   if (split < a.ns8) {
     const int tok0 = split * a.split8;
     const int tok1 = min(a.T8, tok0 + a.split8);
-    const Int8Rows<D> rows{a.kc + (size_t)unit * a.T8 * D, a.vc + (size_t)unit * a.T8 * D};
+    const int8_t* kc = a.kc + (size_t)unit * a.T8 * D;
+    const int8_t* vc = a.vc + (size_t)unit * a.T8 * D;
+    const int nbytes = a.T8 * D;  // < 2^31: checked at the boundary
+    const Int8Rows<D> rows{kc, vc, __builtin_amdgcn_make_buffer_rsrc((void*)kc, (short)0, nbytes, 0x00020000),
+                           __builtin_amdgcn_make_buffer_rsrc((void*)vc, (short)0, nbytes, 0x00020000)};
     const float* ks = a.ks + (size_t)unit * (a.T8 / 32);
     const float* vs = a.vs + (size_t)unit * (a.T8 / 32);
-    // two chunks in flight: the next chunk's loads are issued before this one's math
+    // three chunks in flight per wave: the loads of chunk i+2 are issued before
+    // chunk i's math (unrolled by three, so the register images rotate instead of
+    // being copied).  HBM latency under full load is several microseconds, so the
+    // lookahead, not the math, sets the rate.
+    using Raw = typename DecodeWave<D>::template Raw<true>;
+    auto step = [&](int c, Raw& cur, Raw& ahead) {
+      if (c + 256 < tok1) st.template load<true>(rows, c + 256, ahead);
+      st.template compute<true>(rows, c, cur, ks[c >> 5] * a.scale_log2, vs[c >> 5]);
+    };
     int c0 = tok0 + 32 * w;
     if (c0 < tok1) {
-      typename DecodeWave<D>::template Raw<true> cur, nxt;
-      st.template load<true>(rows, c0, cur);
-      for (; c0 < tok1; c0 += 128) {
-        const bool more = c0 + 128 < tok1;
-        if (more) st.template load<true>(rows, c0 + 128, nxt);
-        st.template compute<true>(rows, c0, cur, ks[c0 >> 5] * a.scale_log2, vs[c0 >> 5]);
-        if (more) cur = nxt;
+      Raw r0, r1, r2;
+      st.template load<true>(rows, c0, r0);
+      if (c0 + 128 < tok1) st.template load<true>(rows, c0 + 128, r1);
+      for (;; c0 += 384) {
+        step(c0, r0, r2);
+        if (c0 + 128 >= tok1) break;
+        step(c0 + 128, r1, r0);
+        if (c0 + 256 >= tok1) break;
+        step(c0 + 256, r2, r1);
+        if (c0 + 384 >= tok1) break;
       }
     }
   } else {

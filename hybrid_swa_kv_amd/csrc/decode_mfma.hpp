@@ -140,6 +140,27 @@ struct DecodeWave {
     const int lane = __lane_id();
     const int hl = lane & 15, gq = lane >> 4;
     constexpr int KV = Raw<INT8>::KV;
+    if constexpr (INT8 && Rows::kBuffer) {
+      // buffer loads: one per-lane offset each for K and V, the chunk start as the
+      // scalar offset and the row / column steps as immediates (no 64-bit address
+      // arithmetic per load)
+      const int soff = c0 * D;
+      const int kl = hl * D + 16 * gq;
+      const int vl = 4 * gq * D + 4 * hl;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+          raw.k[t][kk][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          rows.rk, kl + 16 * t * D + 64 * kk, soff, 0));
+#pragma unroll
+      for (int hv = 0; hv < NK; ++hv)
+#pragma unroll
+        for (int j = 0; j < 4 * NT; ++j)
+          raw.v8[hv][j] = __builtin_amdgcn_raw_buffer_load_b32(
+              rows.rv, vl + (16 * (j >> 2) + (j & 3)) * D + 64 * hv, soff, 0);
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const char* kp = (const char*)rows.kaddr(c0 + 16 * t + hl);
@@ -282,9 +303,22 @@ struct DecodeWave {
       }
     mx = fmaxf(mx, xor16(mx));
     mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m, mx);
-    const float base = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m - base);
+    // Lazy offset: m only moves when a head's maximum grows by more than 8 (a
+    // factor 256 in the log2 domain), so most chunks skip the accumulator rescale;
+    // numerator and denominator always share m.
+    if (__any(mx > m + 8.f)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = (m == kNegInf) ? 0.f : fast_exp2(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int hv = 0; hv < NK; ++hv)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[hv][jj][r] *= alpha;
+      m = m_new;
+    }
+    const float base = (m == kNegInf) ? 0.f : m;
     // P is rounded to bf16 for the MFMA; the normaliser sums the same rounded
     // values, so a row dominated by one key returns that key's value exactly.
     float ps = 0.f;
@@ -299,8 +333,7 @@ struct DecodeWave {
       pw[q] = pack_bf16x2(p0, p1);
       ps += bf16lo(pw[q]) + bf16hi(pw[q]);
     }
-    l = l * alpha + ps;
-    m = m_new;
+    l += ps;
     const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
     for (int hv = 0; hv < NK; ++hv)
@@ -309,7 +342,7 @@ struct DecodeWave {
         f32x4 part = {0.f, 0.f, 0.f, 0.f};
         part = mfma16(va[hv][jj], pb, part);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[hv][jj][r] = fmaf(o[hv][jj][r], alpha, sv * part[r]);
+        for (int r = 0; r < 4; ++r) o[hv][jj][r] = fmaf(sv, part[r], o[hv][jj][r]);
       }
   }
 
@@ -367,8 +400,10 @@ template <int D>
 struct Int8Rows {
   static constexpr bool kAllValid = true;
   static constexpr bool kHasAlt = false;
+  static constexpr bool kBuffer = true;  // loaded through rk / rv
   const int8_t* k;
   const int8_t* v;
+  __amdgpu_buffer_rsrc_t rk, rv;       // the same rows as buffer resources
   const void* kalt = nullptr;
   const void* valt = nullptr;
   __device__ __forceinline__ const void* kaddr(int row) const { return k + (size_t)row * D; }
@@ -384,6 +419,7 @@ template <int D>
 struct Bf16Rows {
   static constexpr bool kAllValid = false;
   static constexpr bool kHasAlt = false;
+  static constexpr bool kBuffer = false;
   const uint16_t* k;
   const uint16_t* v;
   int end;
@@ -404,6 +440,7 @@ template <int D>
 struct RingRows {
   static constexpr bool kAllValid = false;
   static constexpr bool kHasAlt = true;
+  static constexpr bool kBuffer = false;
   const uint16_t* k;
   const uint16_t* v;
   const void* kalt;
