@@ -4,13 +4,14 @@
 // waves take interleaved 16-slot chunks of the ring and run the 16x16x32 MFMA
 // decode of decode_mfma.hpp (heads on the MFMA N axis), then merge their
 // (max, sum, acc) states through LDS behind a single barrier.  Every load of a
-// chunk (ring rows, the new token, q) is issued before anything waits on one,
+// chunk is issued before anything waits on one (q and the new token's rows are
+// fetched once per workgroup into LDS, ahead of the ring loads),
 // so one HBM round trip covers a 128-slot window; longer windows keep the next
 // chunk in flight while the current one is computed.  Small chunks keep each
 // wave's serial work short: the decode of one chunk is the kernel's tail once
 // its data has arrived.  The new token's K/V is written to slot pos mod W and
-// used from k_new/v_new (the stale slot is never read); slots whose position
-// would be negative (ring not yet full) are neither read nor attended.
+// used from k_new/v_new (whatever is read from that slot is discarded); slots
+// whose position would be negative (ring not yet full) are not attended.
 #include "common.hpp"
 #include "decode_mfma.hpp"
 #include "kernels.hpp"
@@ -28,6 +29,7 @@ template <int D>
 __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs a) {
   __shared__ float sm_m[RD_WAVES][16], sm_l[RD_WAVES][16];
   __shared__ float sm_o[RD_WAVES][16][D + 1];
+  __shared__ __attribute__((aligned(16))) uint16_t sm_in[(16 + 2) * D];
 
   const int G = a.Hq / a.Hkv;
   const int HG = G < 16 ? G : 16;  // heads served by this workgroup
@@ -48,17 +50,18 @@ __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs 
   uint16_t* rv = a.ring_v + kvoff * (size_t)W * D;
   const uint16_t* kn = a.k_new + kvoff * D;
   const uint16_t* vn = a.v_new + kvoff * D;
+  // q of the served heads and the new token's K and V rows are staged once per
+  // workgroup in LDS (sm_in: HG*D q values, then D of k_new, then D of v_new):
+  // each thread fetches one 16-byte piece, issued before its ring loads so the
+  // wait for it does not wait for the ring data.
+  const int nq = HG * D / 8, nin = nq + D / 4;
+  const int pi = min(t, nin - 1);
+  const uint16_t* src = pi < nq ? a.q + ((size_t)b * a.Hq + h0) * D + 8 * pi
+                        : pi < nq + D / 8 ? kn + 8 * (pi - nq) : vn + 8 * (pi - nq - D / 8);
+  const uint4 piece = *(const uint4*)src;
+  __builtin_amdgcn_sched_barrier(0);
   DecodeWave<D, true> st;
-  st.init(a.q + ((size_t)b * a.Hq + h0) * D, HG);
-  // slot and position are only needed for the masks: filled in after the loads
-  RingRows<D> rows{rk, rv, kn, vn, W, 0, -1};
-  typename DecodeWave<D, true>::AltRow alt;
-  st.load_alt(rows, alt);
-  // the new token's rows for the append after the barrier, fetched now (every
-  // thread loads a 16-byte piece; threads t < D/8 store theirs)
-  const int tp = t % (D / 8);
-  const uint4 kn_piece = *(const uint4*)(kn + 8 * tp);
-  const uint4 vn_piece = *(const uint4*)(vn + 8 * tp);
+  RingRows<D> rows{rk, rv, sm_in + HG * D, sm_in + HG * D + D, W, 0, -1};
   // software pipelined over the wave's chunks: chunk c+1 is in flight while c is computed
   using Raw = typename DecodeWave<D, true>::template Raw<false>;
   Raw cur, nxt;
@@ -70,6 +73,20 @@ __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs 
   const int slot = (int)((unsigned)max(p, 0) % (unsigned)W);  // branch-free
   rows.slot = slot;
   rows.p = ok ? p : -1;
+  if (t < nin) *(uint4*)(sm_in + 8 * t) = piece;
+  __syncthreads();
+  // append: the first head group's workgroup writes the new token into its slot
+  // now, so the stores complete while the ring loads are in flight.  Any read of
+  // that slot (here or in another head group's workgroup) is replaced by the new
+  // token's rows from LDS, so it does not matter whether it sees old or new bytes.
+  if (ok && hg == 0 && t < D / 8) {
+    *(uint4*)(rk + (size_t)slot * D + 8 * t) = *(const uint4*)(sm_in + HG * D + 8 * t);
+    *(uint4*)(rv + (size_t)slot * D + 8 * t) = *(const uint4*)(sm_in + HG * D + D + 8 * t);
+  }
+  if (ok && hg == 0 && g == 0 && t == 0 && a.slot_out) a.slot_out[b] = slot;
+  st.init(sm_in, HG);
+  typename DecodeWave<D, true>::AltRow alt;
+  st.load_alt(rows, alt);
   int c0 = first;
   for (; c0 + RD_STRIDE < W; c0 += 2 * RD_STRIDE) {
     st.template load<false, 1>(rows, c0 + RD_STRIDE, nxt);
@@ -81,13 +98,6 @@ __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs 
 
   st.stash(sm_m, sm_l, sm_o, w, HG);
   __syncthreads();
-  // append (after every read of the ring in this workgroup): the first head
-  // group's workgroup writes the new token into its slot
-  if (ok && hg == 0 && t < D / 8) {
-    *(uint4*)(rk + (size_t)slot * D + 8 * t) = kn_piece;
-    *(uint4*)(rv + (size_t)slot * D + 8 * t) = vn_piece;
-  }
-  if (ok && hg == 0 && g == 0 && t == 0 && a.slot_out) a.slot_out[b] = slot;
   for (int e = t; e < HG * D; e += RD_THREADS) {
     const int head = e / D, d = e % D;
     float M, Ls;
