@@ -32,9 +32,11 @@ size_t int8_ws_bytes(int B, int Hq, int Hkv, int D, int T8, int Th) {
   return (size_t)B * Hkv * (size_t)(ns8 + nsh) * (size_t)(Hq / Hkv) * (size_t)(D + 2) * sizeof(float);
 }
 
+// block sums [Hq + Hkv][D][nbp] and the score triangle [Hq][nb (nb - 1) / 2], fp64
 size_t bs_ws_bytes(int L, int Hq, int Hkv, int D, int block) {
   const size_t nb = (size_t)L / block;
-  return ((size_t)Hq + Hkv) * nb * D * sizeof(double);
+  const size_t nbp = (nb + 63) / 64 * 64;
+  return (((size_t)Hq + Hkv) * nbp * D + (size_t)Hq * (nb * (nb - 1) / 2)) * sizeof(double);
 }
 
 }  // namespace
@@ -200,8 +202,10 @@ int blocksparse_select_attend(const void* q, const void* k, const void* v, void*
   a.L = L; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.block = block; a.topk = topk;
   a.window = window >= L ? L + 256 : window;
   a.nb = L / block;
+  a.nbp = (a.nb + 63) / 64 * 64;
   a.qsum = (double*)workspace;
-  a.ksum = a.qsum + (size_t)Hq * a.nb * D;
+  a.ksum = a.qsum + (size_t)Hq * a.nbp * D;
+  a.scores = a.ksum + (size_t)Hkv * a.nbp * D;
   a.scale_log2 = log2e_times(scale);
   return finish(hsk::launch_blocksparse(a, (hipStream_t)stream));
 }

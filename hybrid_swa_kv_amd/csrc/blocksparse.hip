@@ -5,20 +5,24 @@
 //  1. bs_sums:   per 64-token block, fp64 sums of Q (all query heads) and of K.
 //                bf16 values have 8-bit significands, so these sums are exact in
 //                fp64 for the value ranges met here and do not depend on order.
-//                Q sums are stored [Hq][nb][D], K sums d-major [Hkv][D][nb] so the
-//                candidate-parallel dot products read 64 consecutive blocks.
-//  2. bs_select: one workgroup per (KV head, query block, up to 4 query heads).
-//                Each lane scores one key block at a time with a sequential fp64
-//                FMA chain over d; the scores sit in LDS.  One wave per query head
-//                then finds the top-k threshold by a 64-step bitwise search over
-//                order-preserving 64-bit keys, takes ties in ascending block order
-//                and writes the chosen blocks ascending (-1 padded).
-//  3. bs_attend: one workgroup (2 waves, 64 query rows = one query block) per
+//                Both are stored d-major, [H][D][nb].
+//  2. bs_scores: per query head, the lower triangle of sumQ * sumK^T (fp64) as a
+//                64 x 64-tiled GEMM with 4 x 4 register tiles: each K sum read from
+//                LDS serves 64 query blocks.  score = sumQ . sumK / 4096 orders
+//                exactly like the mean-vector product (a power-of-two scale), and
+//                each entry is one sequential FMA chain over d.  Rows go to the
+//                workspace as a packed triangle (row qb holds key blocks 0..qb-1).
+//  3. bs_select: one wave per (query head, query block) row.  The top-k threshold
+//                is the largest 64-bit order key T with #{key >= T} >= topk,
+//                found bit by bit: the top 16 bits over all candidates, then the
+//                remaining 48 over the few candidates that share that prefix
+//                (gathered into one key per lane; the full search is kept for
+//                rows with more than 64 such candidates).  Ties take ascending
+//                block order; the chosen blocks are written ascending, -1 padded.
+//  4. bs_attend: one workgroup (2 waves, 64 query rows = one query block) per
 //                (query head, query block); key tiles are the selected blocks
 //                before the window followed by the window's blocks; selected
 //                tiles need no mask, window tiles use the sliding-window mask.
-//                A single LDS tile buffer (next tile staged in registers) keeps
-//                four workgroups resident per CU.
 #include "common.hpp"
 #include "flash_tile.hpp"
 #include "kernels.hpp"
@@ -29,7 +33,6 @@ namespace {
 
 constexpr int BS_BLOCK = 64;
 constexpr int SUM_THREADS = 256;
-constexpr int SEL_THREADS = 256;
 constexpr int SEL_MAXNB = 4096;     // key blocks supported (L <= 262144 at block 64)
 constexpr int AT_THREADS = 128;
 
@@ -54,14 +57,9 @@ __global__ __launch_bounds__(SUM_THREADS) void bs_sums_kernel(BlockSparseArgs a)
     }
     const int e = vi * 8;
     const int h = e / a.D, d = e % a.D;
-    if (isq) {
-      double* dst = a.qsum + ((size_t)h * a.nb + blk) * a.D + d;
+    double* dst = isq ? a.qsum : a.ksum;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) dst[j] = acc[j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) a.ksum[((size_t)h * a.D + d + j) * a.nb + blk] = acc[j];
-    }
+    for (int j = 0; j < 8; ++j) dst[((size_t)h * a.D + d + j) * a.nbp + blk] = acc[j];
   }
 }
 
@@ -70,78 +68,140 @@ __device__ __forceinline__ unsigned long long order_key(double x) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// grid: Hkv * nb * (G / hpw); MAXG * 64 >= nb (key groups held per lane)
-template <int HPW, int MAXG>
-__global__ __launch_bounds__(SEL_THREADS) void bs_select_kernel(BlockSparseArgs a) {
-  __shared__ double qs[256][HPW];               // query block means, [d][head]
-  extern __shared__ double sc_dyn[];            // scores, [head][nb]
-  const int G = a.Hq / a.Hkv;
-  const int ngrp = G / HPW;
-  const int grp = blockIdx.x % ngrp;
-  const int qb = (blockIdx.x / ngrp) % a.nb;
-  const int g = blockIdx.x / (ngrp * a.nb);
-  const int h0 = g * G + grp * HPW;
-  const int D = a.D;
-  const int lane = __lane_id(), w = threadIdx.x >> 6;
-  const double inv = 1.0 / BS_BLOCK;
+// row qb of head h in the packed score triangle (key blocks 0 .. qb-1)
+__device__ __forceinline__ size_t tri_row(const BlockSparseArgs& a, int h, int qb) {
+  return (size_t)h * ((size_t)a.nb * (a.nb - 1) / 2) + (size_t)qb * (qb - 1) / 2;
+}
 
-  for (int e = threadIdx.x; e < HPW * D; e += SEL_THREADS) {
-    const int hh = e / D, d = e % D;
-    qs[d][hh] = a.qsum[((size_t)(h0 + hh) * a.nb + qb) * D + d] * inv;
+constexpr int SC_TILE = 64;     // query blocks x key blocks per workgroup
+constexpr int SC_SLAB = 32;     // d values staged per pass
+
+// grid: Hq * T(T+1)/2 lower-triangle tiles, T = nbp / 64.  Sums are read with
+// row stride nbp, so a tile never leaves its arrays; entries past nb are never
+// stored.
+__global__ __launch_bounds__(256) void bs_scores_kernel(BlockSparseArgs a) {
+  __shared__ __attribute__((aligned(16))) double sq[SC_SLAB][SC_TILE];
+  __shared__ __attribute__((aligned(16))) double sk[SC_SLAB][SC_TILE];
+  const int T = a.nbp / SC_TILE;
+  const int ntri = T * (T + 1) / 2;
+  const int h = blockIdx.x / ntri;
+  const int r = blockIdx.x % ntri;
+  int ti = 0;  // tile row: r = ti (ti + 1) / 2 + tj, tj <= ti
+  while ((ti + 1) * (ti + 2) / 2 <= r) ++ti;
+  const int tj = r - ti * (ti + 1) / 2;
+  const int g = h / (a.Hq / a.Hkv);
+  const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
+  const double* qsrc = a.qsum + (size_t)h * a.D * a.nbp + ti * SC_TILE;
+  const double* ksrc = a.ksum + (size_t)g * a.D * a.nbp + tj * SC_TILE;
+  double acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  for (int d0 = 0; d0 < a.D; d0 += SC_SLAB) {
+    // stage 32 d x 64 blocks of each operand: 4 x 16 bytes per thread per operand
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = i * 256 + t;  // 16-byte unit: d row u / 32, block pair u % 32
+      const int dd = u >> 5, c = (u & 31) * 2;
+      *(double2*)&sq[dd][c] = *(const double2*)(qsrc + (size_t)(d0 + dd) * a.nbp + c);
+      *(double2*)&sk[dd][c] = *(const double2*)(ksrc + (size_t)(d0 + dd) * a.nbp + c);
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int dd = 0; dd < SC_SLAB; ++dd) {
+      const double2 q01 = *(const double2*)&sq[dd][4 * ty], q23 = *(const double2*)&sq[dd][4 * ty + 2];
+      const double2 k01 = *(const double2*)&sk[dd][4 * tx], k23 = *(const double2*)&sk[dd][4 * tx + 2];
+      const double qv[4] = {q01.x, q01.y, q23.x, q23.y}, kv[4] = {k01.x, k01.y, k23.x, k23.y};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(qv[i], kv[j], acc[i][j]);
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  const int n = qb;  // candidates: blocks 0 .. qb-1
-  const double* kcol = a.ksum + (size_t)g * D * a.nb;
-  for (int base = 64 * w; base < n; base += SEL_THREADS) {
-    const int kb = base + lane;
-    double acc[HPW];
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) acc[hh] = 0.0;
-    if (kb < n) {
-      for (int d = 0; d < D; ++d) {
-        const double kv = kcol[(size_t)d * a.nb + kb] * inv;
+  for (int i = 0; i < 4; ++i) {
+    const int qb = ti * SC_TILE + 4 * ty + i;
+    if (qb >= a.nb) continue;
+    double* row = a.scores + tri_row(a, h, qb);
 #pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) acc[hh] = fma(qs[d][hh], kv, acc[hh]);
-      }
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) sc_dyn[(size_t)hh * a.nb + kb] = acc[hh];
+    for (int j = 0; j < 4; ++j) {
+      const int kb = tj * SC_TILE + 4 * tx + j;
+      if (kb < qb) row[kb] = acc[i][j];
     }
   }
-  __syncthreads();
-  if (w >= HPW) return;
-  const int h = h0 + w;
-  int32_t* out = a.sel + ((size_t)h * a.nb + qb) * a.topk;
+}
+
+// grid: Hq * nb / 4, four rows (waves) per workgroup; MAXG * 64 >= nb
+template <int MAXG>
+__global__ __launch_bounds__(256) void bs_select_kernel(BlockSparseArgs a) {
+  __shared__ unsigned long long gather[4][64];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = __lane_id();
+  const int rowid = blockIdx.x * 4 + w;  // h * nb + qb
+  if (rowid >= a.Hq * a.nb) return;
+  const int h = rowid / a.nb, qb = rowid % a.nb;
+  int32_t* out = a.sel + (size_t)rowid * a.topk;
   const int topk = a.topk;
+  const int n = qb;  // candidates: blocks 0 .. qb-1
   if (n <= topk) {
     for (int i = lane; i < topk; i += 64) out[i] = (i < n) ? i : -1;
     return;
   }
-  // top-k threshold: the largest T with #{key >= T} >= topk, found bit by bit.
-  // Each lane keeps its keys (blocks lane, lane+64, ...) in registers; a wave
-  // ballot + popcount counts them, so no step needs a cross-lane reduction.
+  const double* row = a.scores + tri_row(a, h, qb);
   const int ngr = (n + 63) >> 6;
   unsigned long long keys[MAXG];
 #pragma unroll
   for (int i = 0; i < MAXG; ++i) {
     const int kb = i * 64 + lane;
-    keys[i] = (i < ngr && kb < n) ? order_key(sc_dyn[(size_t)w * a.nb + kb]) : 0ull;
+    keys[i] = (i < ngr && kb < n) ? order_key(row[kb]) : 0ull;  // 0 sorts below every key
   }
-  // absent slots hold key 0, which sorts below every real key
-  unsigned long long T = 0;
-  for (int bit = 63; bit >= 0; --bit) {
-    const unsigned long long cand = T | (1ull << bit);
+  auto count_ge = [&](unsigned long long c) {
     int cnt = 0;
 #pragma unroll
     for (int i = 0; i < MAXG; ++i)
-      if (i < ngr) cnt += __popcll(__ballot(keys[i] >= cand));
-    if (cnt >= topk) T = cand;
+      if (i < ngr) cnt += __popcll(__ballot(keys[i] >= c));
+    return cnt;
+  };
+  // 1. the top 16 bits over every candidate
+  unsigned long long T = 0;
+  for (int bit = 63; bit >= 48; --bit) {
+    const unsigned long long cand = T | (1ull << bit);
+    if (count_ge(cand) >= topk) T = cand;
+  }
+  // 2. the low 48 bits: only keys with T's 16-bit prefix can still change a count
+  const unsigned long long pre = T >> 48;
+  const int above = pre == 0xffffull ? 0 : count_ge((pre + 1) << 48);
+  const unsigned long long lt_mask = (1ull << lane) - 1ull;
+  int neq = 0;
+#pragma unroll
+  for (int i = 0; i < MAXG; ++i) {
+    if (i >= ngr) continue;
+    const bool eq = (keys[i] >> 48) == pre && keys[i] != 0ull;
+    const unsigned long long m = __ballot(eq);
+    const int pos = neq + __popcll(m & lt_mask);
+    if (eq && pos < 64) gather[w][pos] = keys[i];
+    neq += __popcll(m);
+  }
+  if (neq <= 64) {
+    __builtin_amdgcn_wave_barrier();
+    const unsigned long long ek = lane < neq ? gather[w][lane] : 0ull;
+    for (int bit = 47; bit >= 0; --bit) {
+      const unsigned long long cand = T | (1ull << bit);
+      if (above + (int)__popcll(__ballot(ek >= cand)) >= topk) T = cand;
+    }
+  } else {  // many candidates share the prefix (ties): search over all of them
+    for (int bit = 47; bit >= 0; --bit) {
+      const unsigned long long cand = T | (1ull << bit);
+      if (count_ge(cand) >= topk) T = cand;
+    }
   }
   int gt = 0;
 #pragma unroll
   for (int i = 0; i < MAXG; ++i)
     if (i < ngr) gt += __popcll(__ballot(keys[i] > T));
   const int need = topk - gt;
-  const unsigned long long lt_mask = (1ull << lane) - 1ull;
   int eq_before = 0, written = 0;
 #pragma unroll
   for (int i = 0; i < MAXG; ++i) {
@@ -154,7 +214,8 @@ __global__ __launch_bounds__(SEL_THREADS) void bs_select_kernel(BlockSparseArgs 
     const int rank = eq_before + __popcll(eqb & lt_mask);
     const bool take = is_gt || (is_eq && rank < need);
     const unsigned long long tb = __ballot(take);
-    if (take) out[written + __popcll(tb & lt_mask)] = kb;
+    const int slot = written + __popcll(tb & lt_mask);
+    if (take && slot < topk) out[slot] = kb;
     written += __popcll(tb);
     eq_before += __popcll(eqb);
   }
@@ -232,24 +293,18 @@ __global__ __launch_bounds__(AT_THREADS) void bs_attend_kernel(BlockSparseArgs a
 }  // namespace
 
 hipError_t launch_blocksparse(const BlockSparseArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(bs_sums_kernel, dim3(2 * a.nb), dim3(SUM_THREADS), 0, s, a);
-  const int G = a.Hq / a.Hkv;
-  const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-  const int sgrid = a.topk > 0 ? a.Hkv * a.nb * (G / hpw) : 0;
-  const size_t dyn = (size_t)hpw * a.nb * sizeof(double);
-  const bool big = a.nb > 2048;
-  if (sgrid == 0) {
-    // no long-range blocks: the attention below is the sliding window alone
-  } else if (hpw == 4) {
-    if (big) hipLaunchKernelGGL((bs_select_kernel<4, 64>), dim3(sgrid), dim3(SEL_THREADS), dyn, s, a);
-    else hipLaunchKernelGGL((bs_select_kernel<4, 32>), dim3(sgrid), dim3(SEL_THREADS), dyn, s, a);
-  } else if (hpw == 2) {
-    if (big) hipLaunchKernelGGL((bs_select_kernel<2, 64>), dim3(sgrid), dim3(SEL_THREADS), dyn, s, a);
-    else hipLaunchKernelGGL((bs_select_kernel<2, 32>), dim3(sgrid), dim3(SEL_THREADS), dyn, s, a);
-  } else {
-    if (big) hipLaunchKernelGGL((bs_select_kernel<1, 64>), dim3(sgrid), dim3(SEL_THREADS), dyn, s, a);
-    else hipLaunchKernelGGL((bs_select_kernel<1, 32>), dim3(sgrid), dim3(SEL_THREADS), dyn, s, a);
+  if (a.topk > 0) {
+    // block sums, the score triangle and the per-row selection
+    hipLaunchKernelGGL(bs_sums_kernel, dim3(2 * a.nb), dim3(SUM_THREADS), 0, s, a);
+    const int T = a.nbp / SC_TILE;
+    hipLaunchKernelGGL(bs_scores_kernel, dim3(a.Hq * T * (T + 1) / 2), dim3(256), 0, s, a);
+    const int sgrid = (a.Hq * a.nb + 3) / 4;
+    if (a.nb > 2048)
+      hipLaunchKernelGGL((bs_select_kernel<64>), dim3(sgrid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((bs_select_kernel<32>), dim3(sgrid), dim3(256), 0, s, a);
   }
+  // with topk == 0 the attention below is the sliding window alone
   const int total = a.Hq * a.nb;
   const int grid = (total + 7) / 8 * 8;
   if (a.D == 128)

@@ -167,7 +167,9 @@ size_t attn_decode_int8kv_workspace_size(int B, int Hq, int Hkv, int D, int T8, 
  * q   [L, Hq,  D] bf16;  k, v [L, Hkv, D] bf16;  out [L, Hq, D] bf16, written
  * sel [Hq, L/block, topk] int32, written
  * block == 64;  L % block == 0;  0 <= topk <= 256;  window >= 1;  scale > 0.
- * workspace: blocksparse_workspace_size(...) bytes (block means, fp64).
+ * workspace: blocksparse_workspace_size(...) bytes: fp64 block sums of Q and K
+ * and the per-head triangle of block scores (Hq * nb * (nb - 1) / 2 doubles,
+ * about 0.5 GB at L = 131072, Hq = 32).
  */
 int blocksparse_select_attend(const void* q, const void* k, const void* v, void* out,
                               int32_t* sel, int L, int Hq, int Hkv, int D,

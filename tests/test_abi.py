@@ -100,7 +100,11 @@ def test_int8_decode_validation(lib):
 def test_blocksparse_validation(lib):
     f = lib.blocksparse_select_attend
     need = lib.blocksparse_workspace_size(131072, 32, 8, 128, 64, 64)
-    assert need == (32 + 8) * 2048 * 128 * 8
+    # fp64 block sums of Q and K ([H][D][nb], nb = 2048 already a multiple of 64)
+    # plus the per-head lower triangle of block scores
+    assert need == ((32 + 8) * 2048 * 128 + 32 * (2048 * 2047 // 2)) * 8
+    # block counts are padded to a multiple of 64 in the sums
+    assert lib.blocksparse_workspace_size(64 * 100, 4, 1, 64, 64, 4) == ((4 + 1) * 128 * 64 + 4 * (100 * 99 // 2)) * 8
     #        q k v out sel L Hq Hkv D block topk win scale ws wsb stream
     assert f(P, P, P, P, None, 1024, 4, 1, 128, 64, 4, 128, 1.0, P, need, None) == NULL
     assert f(P, P, P, P, P, 1000, 4, 1, 128, 64, 4, 128, 1.0, P, need, None) == SHAPE
