@@ -121,6 +121,21 @@ def sparse_pairs(sel, L: int, block: int, W: int) -> int:
     return total
 
 
+def sparse_tile_bytes(sel, L: int, block: int, W: int, Hkv: int, D: int) -> int:
+    """K and V bytes the attention kernel stages for the block-sparse pattern: per
+    (query head, query block) every selected block before the window plus the
+    window's blocks, one 64-token K tile and V tile (bf16) each."""
+    import numpy as np
+
+    Hq, nb, _ = sel.shape
+    qb = np.arange(nb, dtype=np.int64)
+    kw0 = np.maximum(0, qb * block - W + 1) // block                 # first window block
+    tiles = int((qb - kw0 + 1).sum()) * Hq
+    s = sel.astype(np.int64)
+    tiles += int(((s >= 0) & (s < kw0[None, :, None])).sum())
+    return tiles * 2 * block * D * 2
+
+
 class Timer:
     """HIP events around work enqueued on torch's current stream (the library's stream)."""
 
@@ -354,11 +369,14 @@ def main() -> int:
     if "sparse" in rows:
         c = SPARSE
         ms = timer.mean_ms("sparse", args.warmup)
-        pairs = sparse_pairs(ssel.cpu().numpy(), c["L"], c["block"], c["W"])
+        pairs = sparse_pairs(ssel.cpu().numpy(), c["L"], c["block"], c["W"])  # exact, from sel
         flops = 4 * c["D"] * pairs
         tf = flops / (ms * 1e-3) / 1e12
+        sel_np = ssel.cpu().numpy()
+        tb = sparse_tile_bytes(sel_np, c["L"], c["block"], c["W"], c["Hkv"], c["D"])
         res["sparse"] = {"ms": round(ms, 3), "visible_pairs": pairs, "flop": flops, "TFLOP/s": round(tf, 1),
-                         "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+                         "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "kv_tile_bytes": tb, "kv_tile_GB/s": round(tb / (ms * 1e-3) / 1e9, 1)}
 
     line = {
         "metric": METRIC,
