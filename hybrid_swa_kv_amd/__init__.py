@@ -14,4 +14,5 @@ from .api import (  # noqa: F401
     kv_quant_int8_b32,
     swa_decode_ring,
     swa_prefill,
+    swa_window_safe_len,
 )

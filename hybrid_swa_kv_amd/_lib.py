@@ -18,6 +18,7 @@ EXPORTS = (
     "attn_decode_int8kv_workspace_size",
     "blocksparse_select_attend",
     "blocksparse_workspace_size",
+    "swa_window_safe_len",
 )
 
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -32,6 +33,7 @@ _SIGS = {
     "attn_decode_int8kv_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "blocksparse_select_attend": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
     "blocksparse_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
+    "swa_window_safe_len": (_I, [_P, _P, _P, _I, _I, _P]),
 }
 
 _lib = None

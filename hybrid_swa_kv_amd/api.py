@@ -181,3 +181,20 @@ def blocksparse_select_attend(q, k, v, block: int = 64, topk: int = 64, window: 
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(sel) if topk > 0 else None, L, Hq, Hkv, D, block, topk,
         window, scale, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, sel
+
+
+def swa_window_safe_len(slot_pos, match_len, out=None, stream=None):
+    """Longest reusable prefix per sequence whose last W positions keep their SWA slots.
+
+    slot_pos [B, W] int32 (position held by each slot, -1 empty); match_len [B]
+    int32.  Returns safe_len [B] int32.
+    """
+    _need(slot_pos, "slot_pos", torch.int32, 2)
+    _need(match_len, "match_len", torch.int32, 1)
+    B, W = slot_pos.shape
+    if match_len.shape[0] != B:
+        raise ValueError("match_len must have one entry per sequence")
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=slot_pos.device)
+    _check(_lib.load().swa_window_safe_len(_ptr(slot_pos), _ptr(match_len), _ptr(out), B, W, _stream(stream)))
+    return out

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;  // 2: swa_window_safe_len
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -208,6 +208,21 @@ int blocksparse_select_attend(const void* q, const void* k, const void* v, void*
   a.scores = a.ksum + (size_t)Hkv * a.nbp * D;
   a.scale_log2 = log2e_times(scale);
   return finish(hsk::launch_blocksparse(a, (hipStream_t)stream));
+}
+
+int swa_window_safe_len(const int32_t* slot_pos, const int32_t* match_len, int32_t* safe_len, int B, int W,
+                        void* stream) {
+  if (B < 0 || W < 1 || W > 65536) return HSK_ERR_SHAPE;
+  if (B == 0) return HSK_OK;  // nothing is read or written
+  if (!slot_pos || !match_len || !safe_len) return HSK_ERR_NULL;
+  if (!aligned4(slot_pos) || !aligned4(match_len) || !aligned4(safe_len)) return HSK_ERR_ALIGN;
+  hsk::WindowSafeArgs a{};
+  a.slot_pos = slot_pos;
+  a.match_len = match_len;
+  a.safe_len = safe_len;
+  a.B = B;
+  a.W = W;
+  return finish(hsk::launch_window_safe(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

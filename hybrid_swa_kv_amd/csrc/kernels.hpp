@@ -79,6 +79,13 @@ struct BlockSparseArgs {
   float scale_log2;
 };
 
+struct WindowSafeArgs {
+  const int32_t* slot_pos;   // [B, W] position held by each SWA slot, -1 empty
+  const int32_t* match_len;  // [B]
+  int32_t* safe_len;         // [B]
+  int B, W;
+};
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_ring(const RingCopyArgs& a, hipStream_t s);
@@ -87,5 +94,6 @@ hipError_t launch_quant_b32(const QuantArgs& a, hipStream_t s);
 void int8_decode_plan(int B, int Hkv, int T8, int Th, int* split8, int* splith, int* ns8, int* nsh);
 hipError_t launch_int8_decode(const Int8DecodeArgs& a, hipStream_t s);
 hipError_t launch_blocksparse(const BlockSparseArgs& a, hipStream_t s);
+hipError_t launch_window_safe(const WindowSafeArgs& a, hipStream_t s);
 
 }  // namespace hsk

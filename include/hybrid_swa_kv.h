@@ -178,6 +178,25 @@ int blocksparse_select_attend(const void* q, const void* k, const void* v, void*
 
 size_t blocksparse_workspace_size(int L, int Hq, int Hkv, int D, int block, int topk);
 
+/*
+ * swa_window_safe_len — longest reusable prefix whose sliding-window KV survives.
+ *
+ * [MiMo-inf] section 2, prefix cache: under sliding-window layers a token-level
+ * prefix match does not mean the KV is still there; the match is cut to the
+ * "window-safe length", whose last W tokens still have valid SWA slots.  Here a
+ * prefix of length l needs positions max(0, l - W) .. l - 1, and position p is
+ * present when slot p mod W holds p.  safe_len[b] is the largest l <= match_len[b]
+ * whose needed positions are all present (0 if none; match_len < 0 counts as 0).
+ *
+ * slot_pos   [B, W] int32: the position each SWA slot holds, -1 for an empty slot
+ * match_len  [B] int32: the token-level prefix match length
+ * safe_len   [B] int32, written (bit-exact integer output)
+ * Errors: HSK_ERR_SHAPE unless 0 <= B and 1 <= W <= 65536; B == 0 is a no-op
+ * (pointers may then be NULL); otherwise pointers non-NULL and 4-byte aligned.
+ */
+int swa_window_safe_len(const int32_t* slot_pos, const int32_t* match_len, int32_t* safe_len,
+                        int B, int W, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

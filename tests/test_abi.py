@@ -114,3 +114,18 @@ def test_blocksparse_validation(lib):
     assert f(P, P, P, P, P, 64 * 5000, 4, 1, 128, 64, 4, 128, 1.0, P, 1 << 40, None) == UNSUP
     assert f(P, P, P, P, P, 1024, 4, 1, 128, 64, 4, 128, 1.0, P, 10, None) == WS
     assert f(P, P, P, MIS, P, 1024, 4, 1, 128, 64, 4, 128, 1.0, P, need, None) == ALIGN
+
+
+def test_window_safe_validation(lib):
+    f = lib.swa_window_safe_len
+    MIS2 = 4098      # 2-byte aligned only
+    #        slot_pos match out B  W  stream
+    assert f(None, P, P, 4, 8, None) == NULL
+    assert f(P, P, None, 4, 8, None) == NULL
+    assert f(None, None, None, 0, 8, None) == 0  # empty batch
+    assert f(None, None, None, -1, 8, None) == SHAPE
+    assert f(P, P, P, -1, 8, None) == SHAPE
+    assert f(P, P, P, 4, 0, None) == SHAPE
+    assert f(P, P, P, 4, 65537, None) == SHAPE
+    assert f(MIS2, P, P, 4, 8, None) == ALIGN
+    assert f(P, P, P, 0, 8, None) == 0          # empty batch: nothing enqueued
