@@ -11,6 +11,10 @@ One step is one pass over every operation of the path, each at its workload size
   quant   kv_quant_int8_b32 K and V of batch 16, 63488 warm tokens, 8 kv heads
   int8    attn_decode_int8kv batch 16, context 65536 (2048 hot bf16 tokens), 32/8 heads
   sparse  blocksparse_select_attend  L 131072, 32/8 heads, 64-token blocks, top-64, window 1024
+  hybrid70  one decode step of a 70-layer hybrid stack: 60 swa_decode_ring layers
+            (window 128) and 10 full-attention layers (attn_decode_int8kv over an
+            all-bf16 context), batch 32, context 32768, one HIP graph; also the
+            10 full layers alone, to price an all-full step
 
 The JSON line's headline is the ring-decode workload (KV bytes per second of the
 60 ring-decode launches in each step, captured once as a HIP graph and replayed,
@@ -42,6 +46,9 @@ RING = dict(B=32, Hq=32, Hkv=8, D=128, W=128, ctx=32768, layers=60)
 PREFILL = dict(L=131072, Hq=64, Hkv=8, D=128, W=1024)
 INT8 = dict(B=16, Hq=32, Hkv=8, D=128, ctx=65536, hot=2048)
 SPARSE = dict(L=131072, Hq=32, Hkv=8, D=128, block=64, topk=64, W=1024)
+# one decode step of the 70-layer hybrid stack: 60 sliding-window layers (ring,
+# W = 128) and 10 full-attention layers (every 7th), batch 32 at context 32768
+HYBRID = dict(B=32, Hq=32, Hkv=8, D=128, W=128, ctx=32768, layers=70, full_every=7)
 
 
 # HBM traffic of the headline kernel, from the two rocprofv3 --pmc passes recorded
@@ -87,6 +94,16 @@ def ring_bytes_per_call(c=RING) -> int:
     ring = 2 * c["B"] * c["Hkv"] * c["W"] * c["D"] * 2
     q = c["B"] * c["Hq"] * c["D"] * 2
     return ring + 2 * q + 2 * c["B"] * c["Hkv"] * c["D"] * 2
+
+
+def full_decode_bytes(c=HYBRID) -> int:
+    """One full-attention decode layer: K and V of the whole context, q read, out write."""
+    return 2 * c["B"] * c["Hkv"] * c["ctx"] * c["D"] * 2 + 2 * c["B"] * c["Hq"] * c["D"] * 2
+
+
+def hybrid_layers(c=HYBRID):
+    """Layer kinds of the stack in order: True for a full-attention layer."""
+    return [(i % c["full_every"]) == c["full_every"] - 1 for i in range(c["layers"])]
 
 
 def int8_decode_bytes(c=INT8) -> int:
@@ -200,7 +217,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--rows", default="ring,swa,full,quant,int8,sparse")
+    ap.add_argument("--rows", default="ring,swa,full,quant,int8,sparse,hybrid70")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -301,6 +318,54 @@ def main() -> int:
                           dtype=torch.uint8, device=dev)
         work["sparse"] = lambda: hsk.blocksparse_select_attend(sq, sk, sv, c["block"], c["topk"], c["W"],
                                                                out=sout, sel=ssel, workspace=sws)
+    if "hybrid70" in rows:
+        c = HYBRID
+        kinds = hybrid_layers()
+        hpos = torch.full((c["B"],), c["ctx"] - 1, dtype=torch.int32, device=dev)
+        hslots = torch.empty(c["B"], dtype=torch.int32, device=dev)
+        hws = torch.empty(hsk.attn_decode_int8kv_workspace_size(c["B"], c["Hq"], c["Hkv"], c["D"], 0, c["ctx"]),
+                          dtype=torch.uint8, device=dev)
+        hlayers = []
+        for i, full in enumerate(kinds):
+            q = synth.normal_gpu(6, 100 + i, (c["B"], c["Hq"], c["D"]))
+            if full:   # the layer's whole K/V cache, [B, Hkv, ctx, D]
+                kf = synth.normal_gpu(6, 1000 + 2 * i, (c["B"], c["Hkv"], c["ctx"], c["D"]))
+                vf = synth.normal_gpu(6, 1001 + 2 * i, (c["B"], c["Hkv"], c["ctx"], c["D"]))
+                hlayers.append(("full", q, kf, vf, torch.empty_like(q)))
+            else:      # the layer's ring and the new token's K/V
+                rk = synth.normal_gpu(6, 3000 + 2 * i, (c["B"], c["Hkv"], c["W"], c["D"]))
+                rv = synth.normal_gpu(6, 3001 + 2 * i, (c["B"], c["Hkv"], c["W"], c["D"]))
+                kn = synth.normal_gpu(6, 5000 + 2 * i, (c["B"], c["Hkv"], c["D"]))
+                vn = synth.normal_gpu(6, 5001 + 2 * i, (c["B"], c["Hkv"], c["D"]))
+                hlayers.append(("swa", q, kn, vn, rk, rv, torch.empty_like(q)))
+
+        def run_layer(layer):
+            if layer[0] == "full":
+                _, q, kf, vf, o = layer
+                hsk.attn_decode_int8kv(q, None, None, None, None, kf, vf, out=o, workspace=hws)
+            else:
+                _, q, kn, vn, rk, rv, o = layer
+                hsk.swa_decode_ring(q, kn, vn, rk, rv, hpos, out=o, slot_out=hslots)
+
+        def capture(layers):
+            for ly in layers:
+                run_layer(ly)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for ly in layers:
+                    run_layer(ly)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for ly in layers:
+                    run_layer(ly)
+            return g
+
+        hybrid_graph = capture(hlayers)
+        full_graph = capture([ly for ly in hlayers if ly[0] == "full"])   # the 10 full layers alone
+        work["hybrid70"] = hybrid_graph.replay
     if args.calib_copy:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -377,6 +442,27 @@ def main() -> int:
         res["sparse"] = {"ms": round(ms, 3), "visible_pairs": pairs, "flop": flops, "TFLOP/s": round(tf, 1),
                          "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                          "kv_tile_bytes": tb, "kv_tile_GB/s": round(tb / (ms * 1e-3) / 1e9, 1)}
+
+    if "hybrid70" in rows:
+        c = HYBRID
+        ms = timer.mean_ms("hybrid70", args.warmup)
+        nfull = sum(hybrid_layers())
+        nswa = c["layers"] - nfull
+        step_bytes = nswa * ring_bytes_per_call() + nfull * full_decode_bytes()
+        # the full layers alone, to price an all-full 70-layer step
+        ft = Timer(torch)
+        for _ in range(3):
+            ft.run("full", full_graph.replay)
+        torch.cuda.synchronize()
+        full_us = ft.mean_ms("full", 1) * 1e3 / nfull
+        all_full_bytes = c["layers"] * full_decode_bytes()
+        gbs = step_bytes / (ms * 1e-3) / 1e9
+        res["hybrid70"] = {"ms_per_step": round(ms, 4), "layers": f"{nswa} swa (W {c['W']}) + {nfull} full",
+                           "bytes_per_step": step_bytes, "GB/s": round(gbs, 1),
+                           "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                           "full_layer_us": round(full_us, 2),
+                           "kv_bytes_ratio_vs_all_full": round(step_bytes / all_full_bytes, 4),
+                           "time_ratio_vs_all_full": round(ms * 1e3 / (c["layers"] * full_us), 4)}
 
     line = {
         "metric": METRIC,
