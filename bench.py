@@ -8,6 +8,8 @@ One step is one pass over every operation of the path, each at its workload size
                             sliding-window layer of a 70-layer hybrid stack)
   swa     swa_prefill       L 131072, 64 q / 8 kv heads, head_dim 128, window 1024
   full    swa_prefill       same shape, full causal
+  chunk4096 / chunk8192  swa_prefill_chunk: the window prefill as 32 (16) chunks,
+            each continuing from the ring the previous chunk left
   quant   kv_quant_int8_b32 K and V of batch 16, 63488 warm tokens, 8 kv heads
   int8    attn_decode_int8kv batch 16, context 65536 (2048 hot bf16 tokens), 32/8 heads
   sparse  blocksparse_select_attend  L 131072, 32/8 heads, 64-token blocks, top-64, window 1024
@@ -217,7 +219,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--rows", default="ring,swa,full,quant,int8,sparse,hybrid70")
+    ap.add_argument("--rows", default="ring,swa,full,chunk4096,chunk8192,quant,int8,sparse,hybrid70")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -272,7 +274,7 @@ def main() -> int:
         with torch.cuda.graph(ring_graph):
             ring_step()
         work["ring"] = ring_graph.replay
-    if "swa" in rows or "full" in rows:
+    if any(r in rows for r in ("swa", "full", "chunk4096", "chunk8192")):
         c = PREFILL
         pq = synth.normal_gpu(3, synth.Q, (c["L"], c["Hq"], c["D"]))
         pk = synth.normal_gpu(3, synth.K, (c["L"], c["Hkv"], c["D"]))
@@ -282,6 +284,20 @@ def main() -> int:
             work["swa"] = lambda: hsk.swa_prefill(pq, pk, pv, PREFILL["W"], out=pout)
         if "full" in rows:
             work["full"] = lambda: hsk.swa_prefill(pq, pk, pv, 0, out=pout)
+        for C in (4096, 8192):
+            name = f"chunk{C}"
+            if name in rows:
+                # the window prefill in chunks of C tokens, each continuing from the ring
+                cring_k = torch.empty((1, c["Hkv"], c["W"], c["D"]), dtype=torch.bfloat16, device=dev)
+                cring_v = torch.empty_like(cring_k)
+                cq, ck, cv, co = pq[None], pk[None], pv[None], pout[None]
+                chunk_outs = [torch.empty_like(cq[:, p0:p0 + C]) for p0 in range(0, c["L"], C)]
+
+                def chunk_run(C=C, rk=cring_k, rv=cring_v, outs=chunk_outs):
+                    for i, p0 in enumerate(range(0, PREFILL["L"], C)):
+                        hsk.swa_prefill_chunk(cq[:, p0:p0 + C], ck[:, p0:p0 + C], cv[:, p0:p0 + C], rk, rv, p0,
+                                              out=outs[i])
+                work[name] = chunk_run
     if "quant" in rows or "int8" in rows:
         c = INT8
         t8 = c["ctx"] - c["hot"]
@@ -421,6 +437,15 @@ def main() -> int:
                          "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
     if "swa" in rows and "full" in rows:
         res["full_over_swa_flop_ratio"] = round(res["full"]["flop"] / res["swa"]["flop"], 4)
+    for C in (4096, 8192):
+        name = f"chunk{C}"
+        if name in rows:
+            c = PREFILL
+            ms = timer.mean_ms(name, args.warmup)
+            flops = 4 * c["D"] * c["Hq"] * pairs_prefill(c["L"], c["W"])
+            tf = flops / (ms * 1e-3) / 1e12
+            res[name] = {"ms": round(ms, 3), "chunks": c["L"] // C, "flop": flops, "TFLOP/s": round(tf, 1),
+                         "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
     if "quant" in rows:
         ms = timer.mean_ms("quant", args.warmup)
         gbs = int8_quant_bytes() / (ms * 1e-3) / 1e9

@@ -14,5 +14,6 @@ from .api import (  # noqa: F401
     kv_quant_int8_b32,
     swa_decode_ring,
     swa_prefill,
+    swa_prefill_chunk,
     swa_window_safe_len,
 )

@@ -19,6 +19,7 @@ EXPORTS = (
     "blocksparse_select_attend",
     "blocksparse_workspace_size",
     "swa_window_safe_len",
+    "swa_prefill_chunk",
 )
 
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -34,6 +35,7 @@ _SIGS = {
     "blocksparse_select_attend": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
     "blocksparse_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "swa_window_safe_len": (_I, [_P, _P, _P, _I, _I, _P]),
+    "swa_prefill_chunk": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
 }
 
 _lib = None

@@ -32,6 +32,26 @@ def _stream(stream):
     return s.cuda_stream
 
 
+def _out(t, name, dtype, shape, device):
+    """A caller-supplied output must be exactly what the kernel writes (a contiguous
+    GPU tensor of this dtype and shape); None allocates one."""
+    shape = tuple(int(x) for x in shape)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _need(t, name, dtype)
+    if tuple(t.shape) != shape:
+        raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+    return t
+
+
+def _scratch(t, name, nbytes, device):
+    """Workspace: a contiguous GPU tensor of at least nbytes (None allocates one)."""
+    if t is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    _need(t, name)
+    return t
+
+
 def _need(t, name, dtype=None, ndim=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -61,8 +81,7 @@ def swa_prefill(q, k, v, window: int, scale: float | None = None, out=None, ring
         raise ValueError("dtype must be bfloat16 or float32")
     B, L, Hq, D = (1, *q.shape) if squeeze else q.shape
     Hkv = k.shape[-2]
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out(out, "out", q.dtype, q.shape, q.device)
     _need(out, "out", dtype)
     W = 0
     if ring_k is not None or ring_v is not None:
@@ -91,10 +110,8 @@ def swa_decode_ring(q, k_new, v_new, ring_k, ring_v, pos, scale: float | None = 
     _need(pos, "pos", torch.int32, 1)
     B, Hq, D = q.shape
     Hkv, W = ring_k.shape[1], ring_k.shape[2]
-    if out is None:
-        out = torch.empty_like(q)
-    if slot_out is None:
-        slot_out = torch.empty(B, dtype=torch.int32, device=q.device)
+    out = _out(out, "out", q.dtype, q.shape, q.device)
+    slot_out = _out(slot_out, "slot_out", torch.int32, (B,), q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(_lib.load().swa_decode_ring(
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(ring_k), _ptr(ring_v), _ptr(pos), _ptr(out), _ptr(slot_out),
@@ -109,10 +126,8 @@ def kv_quant_int8_b32(x, codes=None, scales=None, stream=None):
     """
     _need(x, "x", torch.bfloat16, 4)
     B, Hkv, T, D = x.shape
-    if codes is None:
-        codes = torch.empty(x.shape, dtype=torch.int8, device=x.device)
-    if scales is None:
-        scales = torch.empty((B, Hkv, T // 32), dtype=torch.float32, device=x.device)
+    codes = _out(codes, "codes", torch.int8, x.shape, x.device)
+    scales = _out(scales, "scales", torch.float32, (B, Hkv, T // 32), x.device)
     _check(_lib.load().kv_quant_int8_b32(_ptr(x), _ptr(codes), _ptr(scales), B, Hkv, T, D, _stream(stream)))
     return codes, scales
 
@@ -139,11 +154,9 @@ def attn_decode_int8kv(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot, sc
         _need(v_codes, "v_codes", torch.int8, 4)
         _need(k_scales, "k_scales", torch.float32, 3)
         _need(v_scales, "v_scales", torch.float32, 3)
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out(out, "out", torch.bfloat16, q.shape, q.device)
     need = attn_decode_int8kv_workspace_size(B, Hq, Hkv, D, T8, Th)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    workspace = _scratch(workspace, "workspace", need, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(_lib.load().attn_decode_int8kv(
         _ptr(q), _ptr(k_codes) if T8 else None, _ptr(k_scales) if T8 else None,
@@ -169,13 +182,10 @@ def blocksparse_select_attend(q, k, v, block: int = 64, topk: int = 64, window: 
     _need(v, "v", torch.bfloat16, 3)
     L, Hq, D = q.shape
     Hkv = k.shape[1]
-    if out is None:
-        out = torch.empty_like(q)
-    if sel is None:
-        sel = torch.empty((Hq, L // block, topk), dtype=torch.int32, device=q.device)
+    out = _out(out, "out", torch.bfloat16, q.shape, q.device)
+    sel = _out(sel, "sel", torch.int32, (Hq, L // block, topk), q.device)
     need = blocksparse_workspace_size(L, Hq, Hkv, D, block, topk)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    workspace = _scratch(workspace, "workspace", need, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(_lib.load().blocksparse_select_attend(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(sel) if topk > 0 else None, L, Hq, Hkv, D, block, topk,
@@ -194,7 +204,27 @@ def swa_window_safe_len(slot_pos, match_len, out=None, stream=None):
     B, W = slot_pos.shape
     if match_len.shape[0] != B:
         raise ValueError("match_len must have one entry per sequence")
-    if out is None:
-        out = torch.empty(B, dtype=torch.int32, device=slot_pos.device)
+    out = _out(out, "out", torch.int32, (B,), slot_pos.device)
     _check(_lib.load().swa_window_safe_len(_ptr(slot_pos), _ptr(match_len), _ptr(out), B, W, _stream(stream)))
+    return out
+
+
+def swa_prefill_chunk(q, k, v, ring_k, ring_v, pos0: int, scale: float | None = None, out=None, stream=None):
+    """Sliding-window prefill of a chunk at positions pos0 .. pos0+C-1, continuing from a ring.
+
+    q [B, C, Hq, D]; k, v [B, C, Hkv, D]; ring_k, ring_v [B, Hkv, W, D] (bf16; on
+    entry positions before pos0, updated in place to the last W positions).
+    The window is the ring size W.  Returns out [B, C, Hq, D].
+    """
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(ring_k, "ring_k", torch.bfloat16, 4)
+    _need(ring_v, "ring_v", torch.bfloat16, 4)
+    B, C, Hq, D = q.shape
+    Hkv, W = ring_k.shape[1], ring_k.shape[2]
+    out = _out(out, "out", q.dtype, q.shape, q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(_lib.load().swa_prefill_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ring_k), _ptr(ring_v),
+                                         B, C, Hq, Hkv, D, W, int(pos0), scale, _stream(stream)))
     return out

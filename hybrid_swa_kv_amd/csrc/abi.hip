@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;  // 2: swa_window_safe_len
+constexpr int kAbiVersion = 3;  // 2: swa_window_safe_len, 3: swa_prefill_chunk
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -93,6 +93,41 @@ int swa_prefill(const void* q, const void* k, const void* v, void* out, int B, i
     e = hsk::launch_prefill_ring(r, s);
   }
   return finish(e);
+}
+
+int swa_prefill_chunk(const void* q, const void* k, const void* v, void* out, void* ring_k, void* ring_v, int B,
+                      int C, int Hq, int Hkv, int D, int W, int pos0, float scale, void* stream) {
+  if (!q || !k || !v || !out || !ring_k || !ring_v) return HSK_ERR_NULL;
+  if (B <= 0 || C <= 0 || pos0 < 0) return HSK_ERR_SHAPE;
+  if (int rc = check_heads(Hq, Hkv, D)) return rc;
+  if (W < 64 || W > 65536 || W % 64 != 0 || pos0 % 64 != 0) return HSK_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || scale <= 0.f) return HSK_ERR_SHAPE;
+  if ((long long)C > (1ll << 30) || (long long)B * C * Hq > (1ll << 31) - 1) return HSK_ERR_SHAPE;
+  if ((long long)pos0 + C > (1ll << 30)) return HSK_ERR_SHAPE;
+  if ((long long)C * Hkv * D * 2 >= (1ll << 32)) return HSK_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(ring_k) ||
+      !aligned16(ring_v))
+    return HSK_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  hsk::PrefillArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)out;
+  a.B = B; a.L = C; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
+  a.window = W;
+  a.scale = scale;
+  a.scale_log2 = log2e_times(scale);
+  a.ring_k = (const uint16_t*)ring_k;
+  a.ring_v = (const uint16_t*)ring_v;
+  a.pos0 = pos0;
+  hipError_t e = hsk::launch_prefill_bf16(a, s);
+  if (e != hipSuccess) return HSK_ERR_HIP;
+  // then (stream order: after every read of the old ring) the ring keeps the last W positions
+  hsk::RingCopyArgs r{};
+  r.k = k; r.v = v; r.ring_k = ring_k; r.ring_v = ring_v;
+  r.B = B; r.L = C; r.Hkv = Hkv; r.W = W; r.row_bytes = D * 2; r.pos0 = pos0;
+  return finish(hsk::launch_prefill_ring(r, s));
 }
 
 int swa_decode_ring(const void* q, const void* k_new, const void* v_new, void* ring_k, void* ring_v,

@@ -131,6 +131,18 @@ struct TileDma {
       voff[i] = (unsigned)row * row_bytes + chunk * 16;
     }
   }
+  // one of two staging descriptors, chosen by value (a wave-uniform choice); a
+  // choice by reference would send both descriptors through scratch memory
+  __device__ __forceinline__ static TileDma pick(bool first, const TileDma& x, const TileDma& y) {
+    TileDma r;
+    r.rk = first ? x.rk : y.rk;
+    r.rv = first ? x.rv : y.rv;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) r.voff[i] = first ? x.voff[i] : y.voff[i];
+    r.tile_bytes = first ? x.tile_bytes : y.tile_bytes;
+    r.wave_lds = x.wave_lds;
+    return r;
+  }
   // start loading tile kt into the LDS buffer kv_lds (K then V, TILE bytes each)
   __device__ __forceinline__ void issue(int kt, char* kv_lds) const {
     const unsigned so = (unsigned)kt * tile_bytes;

@@ -18,6 +18,12 @@ struct PrefillArgs {
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
   int nqb, total;    // filled by the launcher
+  // chunk mode (ring_k != nullptr): the L rows are positions pos0 .. pos0+L-1 and
+  // positions before pos0 are read from the ring [B, Hkv, window, D] at slot
+  // position mod window (pos0 and window multiples of 64)
+  const uint16_t* ring_k;
+  const uint16_t* ring_v;
+  int pos0;
 };
 
 struct RingCopyArgs {
@@ -26,6 +32,7 @@ struct RingCopyArgs {
   void* ring_k;   // [B, Hkv, W, D]
   void* ring_v;
   int B, L, Hkv, W, row_bytes;
+  int pos0;       // absolute position of row 0 of k / v
 };
 
 struct RingDecodeArgs {

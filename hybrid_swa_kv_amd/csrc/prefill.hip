@@ -21,10 +21,13 @@ namespace {
 constexpr int PF_BM = 128;
 constexpr int PF_THREADS = 256;
 
-template <int D>
-__global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
+// CHUNK: the rows are positions pos0 .. pos0+L-1 of a longer sequence; key
+// tiles before pos0 are fetched from the ring (slot tile (position mod W) / 64),
+// later ones from the chunk's own K/V.  pos0 and W are multiples of 64, so no
+// tile straddles the two sources.
+template <int D, bool CHUNK>
+__device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
   using C = FtCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * C::TILE];
 
   // XCD-aware order: consecutive logical units share (b, kv head, query block)
   // and land on the same XCD (workgroups are dealt round-robin over 8 XCDs).
@@ -45,29 +48,44 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(PrefillArgs
   const int q0 = qblk * PF_BM;
   const int lane = __lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
-  const int r0 = q0 + 32 * w;        // first row of this wave
-  const int row = r0 + (lane & 31);  // this lane's query row
+  const int base = CHUNK ? a.pos0 : 0;  // position of row 0
+  const int r0 = base + q0 + 32 * w;    // position of this wave's first row
+  const int row = r0 + (lane & 31);     // this lane's query position
+  const int rrow = row - base;          // ... as a row of q / out
 
-  const int k_lo = max(0, q0 - W + 1);
-  const int k_hi = min(L, q0 + PF_BM) - 1;
+  const int k_lo = max(0, base + q0 - W + 1);
+  const int k_hi = base + min(L, q0 + PF_BM) - 1;
   const int kt0 = k_lo / FT_BN;
   const int ntiles = k_hi / FT_BN - kt0 + 1;
 
   FlashWave<D> fw;
-  fw.init(row < L ? a.q + ((size_t)(b * (size_t)L + row) * a.Hq + h) * D : nullptr);
+  fw.init(rrow < L ? a.q + ((size_t)(b * (size_t)L + rrow) * a.Hq + h) * D : nullptr);
 
   const uint16_t* kbase = a.k + ((size_t)b * L * a.Hkv + g) * D;
   const uint16_t* vbase = a.v + ((size_t)b * L * a.Hkv + g) * D;
   TileDma<D, PF_THREADS> dma;
   dma.init(kbase, vbase, (unsigned)(a.Hkv * D * 2), L, w);
-  dma.issue(kt0, smem);
+  TileDma<D, PF_THREADS> dring;  // chunk mode: the ring of (b, g), rows of D values
+  if (CHUNK) {
+    const size_t roff = ((size_t)b * a.Hkv + g) * W * D;
+    dring.init(a.ring_k + roff, a.ring_v + roff, (unsigned)(D * 2), W, w);
+  }
+  auto issue = [&](int kt, char* buf) {
+    if (CHUNK) {
+      const bool ring = kt * FT_BN < base;
+      TileDma<D, PF_THREADS>::pick(ring, dring, dma).issue(ring ? (kt * FT_BN % W) / FT_BN : kt - base / FT_BN, buf);
+    } else {
+      dma.issue(kt, buf);
+    }
+  };
+  issue(kt0, smem);
 
   // unrolled by two so each buffer's LDS offsets are compile-time constants
   auto step = [&](int it, char* cur, char* nxt) {
     wait_vmem();      // this wave's part of tile it has landed
     __syncthreads();  // ... everyone's has, and tile it-1's buffer is free
     const int kt = kt0 + it;
-    if (it + 1 < ntiles) dma.issue(kt + 1, nxt);
+    if (it + 1 < ntiles) issue(kt + 1, nxt);
     fw.tile(cur, cur + C::TILE, kt * FT_BN, r0, row, W, false, a.scale_log2);
   };
   int it = 0;
@@ -76,7 +94,19 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(PrefillArgs
     step(it + 1, smem + 2 * C::TILE, smem);
   }
   if (it < ntiles) step(it, smem, smem + 2 * C::TILE);
-  fw.store(row < L ? a.o + ((size_t)(b * (size_t)L + row) * a.Hq + h) * D : nullptr);
+  fw.store(rrow < L ? a.o + ((size_t)(b * (size_t)L + rrow) * a.Hq + h) * D : nullptr);
+}
+
+template <int D>
+__global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * FtCfg<D>::TILE];
+  prefill_body<D, false>(a, smem);
+}
+
+template <int D>
+__global__ __launch_bounds__(PF_THREADS, 2) void prefill_chunk_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * FtCfg<D>::TILE];
+  prefill_body<D, true>(a, smem);
 }
 
 // fp32: one thread per (b, row, head); exact fp32 arithmetic with expf.
@@ -134,7 +164,7 @@ __global__ void prefill_ring_kernel(RingCopyArgs a) {
   const int g = (int)(t % a.Hkv);
   const int b = (int)(t / a.Hkv);
   const int p = a.L - n + i;
-  const int slot = p % a.W;
+  const int slot = (a.pos0 + p) % a.W;
   const size_t src = (((size_t)b * a.L + p) * a.Hkv + g) * a.row_bytes + (size_t)c * 16;
   const size_t dst = (((size_t)b * a.Hkv + g) * a.W + slot) * a.row_bytes + (size_t)c * 16;
   *(uint4*)((char*)a.ring_k + dst) = *(const uint4*)((const char*)a.k + src);
@@ -148,10 +178,14 @@ hipError_t launch_prefill_bf16(const PrefillArgs& in, hipStream_t stream) {
   a.nqb = (a.L + PF_BM - 1) / PF_BM;
   a.total = a.B * a.Hq * a.nqb;
   const int grid = (a.total + 7) / 8 * 8;
-  if (a.D == 128)
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(grid), dim3(PF_THREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(grid), dim3(PF_THREADS), 0, stream, a);
+  const bool chunk = a.ring_k != nullptr;
+  if (a.D == 128) {
+    if (chunk) hipLaunchKernelGGL(prefill_chunk_kernel<128>, dim3(grid), dim3(PF_THREADS), 0, stream, a);
+    else hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(grid), dim3(PF_THREADS), 0, stream, a);
+  } else {
+    if (chunk) hipLaunchKernelGGL(prefill_chunk_kernel<64>, dim3(grid), dim3(PF_THREADS), 0, stream, a);
+    else hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(grid), dim3(PF_THREADS), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -79,6 +79,30 @@ int swa_prefill(const void* q, const void* k, const void* v, void* out,
                 void* ring_k, void* ring_v, int ring_w, void* stream);
 
 /*
+ * swa_prefill_chunk — one chunk of a sliding-window prefill, continuing from a ring.
+ *
+ * [K25-arch] section 4.2 prefills long inputs in chunks (prefill_chunk_size
+ * 4096); [MiMo-inf] section 2 keeps a sliding-window layer's KV in a W-slot
+ * ring (slot = position mod W).  The chunk holds positions pos0 .. pos0+C-1 of
+ * every sequence; query i attends positions max(0, i-W+1) .. i; positions below
+ * pos0 are read from the ring, which on entry holds positions max(0, pos0-W) ..
+ * pos0-1 at slot position mod W.  On return the ring holds positions
+ * max(0, pos0+C-W) .. pos0+C-1 (the chunk's rows written after its attention,
+ * in stream order).  bf16 only.
+ *
+ * q, out       [B, C, Hq, D] bf16 (token-major, as in swa_prefill)
+ * k, v         [B, C, Hkv, D] bf16, the chunk's own K/V
+ * ring_k/v     [B, Hkv, W, D] bf16, read and updated in place
+ * pos0         position of the chunk's first row; W the window and ring size
+ * Limits: pos0 and W multiples of 64, 64 <= W <= 65536, else HSK_ERR_UNSUPPORTED;
+ * scale > 0 and finite; pointers 16-byte aligned.
+ */
+int swa_prefill_chunk(const void* q, const void* k, const void* v, void* out,
+                      void* ring_k, void* ring_v,
+                      int B, int C, int Hq, int Hkv, int D, int W, int pos0, float scale,
+                      void* stream);
+
+/*
  * swa_decode_ring — one decode token per sequence against a sliding-window ring.
  *
  * [MiMo-inf] section 2 ("dual pools"): the SWA pool holds exactly W tokens per

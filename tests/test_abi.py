@@ -129,3 +129,16 @@ def test_window_safe_validation(lib):
     assert f(P, P, P, 4, 65537, None) == SHAPE
     assert f(MIS2, P, P, 4, 8, None) == ALIGN
     assert f(P, P, P, 0, 8, None) == 0          # empty batch: nothing enqueued
+
+
+def test_prefill_chunk_validation(lib):
+    f = lib.swa_prefill_chunk
+    #        q k v out rk rv B C  Hq Hkv D  W   pos0 scale stream
+    assert f(P, P, P, P, None, P, 1, 64, 8, 2, 128, 128, 0, 1.0, None) == NULL
+    assert f(P, P, P, P, P, P, 0, 64, 8, 2, 128, 128, 0, 1.0, None) == SHAPE
+    assert f(P, P, P, P, P, P, 1, 64, 8, 2, 128, 128, -64, 1.0, None) == SHAPE
+    assert f(P, P, P, P, P, P, 1, 64, 8, 2, 128, 100, 0, 1.0, None) == UNSUP     # W % 64
+    assert f(P, P, P, P, P, P, 1, 64, 8, 2, 128, 128, 32, 1.0, None) == UNSUP    # pos0 % 64
+    assert f(P, P, P, P, P, P, 1, 64, 8, 2, 96, 128, 0, 1.0, None) == UNSUP      # head_dim
+    assert f(P, P, P, P, P, P, 1, 64, 8, 2, 128, 128, 0, 0.0, None) == SHAPE
+    assert f(P, P, P, MIS, P, P, 1, 64, 8, 2, 128, 128, 0, 1.0, None) == ALIGN

@@ -1,0 +1,67 @@
+"""GPU parity: swa_prefill_chunk, chunk after chunk, carrying the ring."""
+
+import numpy as np
+import pytest
+import torch
+
+import hybrid_swa_kv_amd as hsk
+import oracle
+from hybrid_swa_kv_amd import synth
+from tests.helpers import announce, bf16_excess, f64, gpu_bf16, max_abs, out_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_chunks(seed, B, L, C, Hq, Hkv, D, W, check_rows=None):
+    q = synth.token_major(seed, synth.Q, L, Hq, D, B=B)
+    k = synth.token_major(seed, synth.K, L, Hkv, D, B=B)
+    v = synth.token_major(seed, synth.V, L, Hkv, D, B=B)
+    dq, dk, dv = gpu_bf16(q), gpu_bf16(k), gpu_bf16(v)
+    # slots never written hold garbage: they must never be read
+    rk = gpu_bf16(synth.head_major(seed, synth.MISC, B, Hkv, W, D))
+    rv = gpu_bf16(synth.head_major(seed, synth.MISC + 1, B, Hkv, W, D))
+    out = torch.empty_like(dq)
+    for pos0 in range(0, L, C):
+        c = min(C, L - pos0)
+        sl = slice(pos0, pos0 + c)
+        oc = hsk.swa_prefill_chunk(dq[:, sl].contiguous(), dk[:, sl].contiguous(), dv[:, sl].contiguous(), rk, rv,
+                                   pos0)
+        out[:, sl] = oc
+    torch.cuda.synchronize()
+    return q, k, v, out, rk, rv
+
+
+@pytest.mark.parametrize("L,C,W,Hq,Hkv,D", [
+    (1636, 512, 1024, 8, 2, 128),   # window longer than a chunk, ragged last chunk
+    (1636, 512, 128, 8, 2, 128),
+    (1000, 256, 128, 4, 4, 64),
+    (700, 128, 64, 16, 1, 128),
+])
+def test_chunked_prefill_equals_one_shot(L, C, W, Hq, Hkv, D):
+    announce("prefill_chunk", L=L, C=C, W=W, Hq=Hq, Hkv=Hkv, D=D)
+    B = 2
+    q, k, v, out, rk, rv = _run_chunks(800 + W + C, B, L, C, Hq, Hkv, D, W)
+    ref = oracle.swa_prefill(f64(q), f64(k), f64(v), W)
+    ex = bf16_excess(out_f64(out), ref)
+    assert ex <= 0, (ex, max_abs(out_f64(out), ref))
+    # the ring holds the last W positions, bit for bit
+    held = oracle.ring_positions(L - 1, W)
+    got_k, got_v = out_f64(rk), out_f64(rv)
+    for s in range(W):
+        assert np.array_equal(got_k[:, :, s], f64(k)[:, held[s]])
+        assert np.array_equal(got_v[:, :, s], f64(v)[:, held[s]])
+
+
+def test_chunked_prefill_131072_in_4096_chunks_sampled():
+    """The hybrid-layer prefill shape (L 131072, 64/8 heads, window 1024) as 32
+    chunks of 4096; sampled rows of several chunks against the oracle."""
+    announce("prefill_chunk_131072")
+    L, C, W, Hq, Hkv, D = 131072, 4096, 1024, 64, 8, 128
+    q, k, v, out, rk, rv = _run_chunks(880, 1, L, C, Hq, Hkv, D, W)
+    rows = np.array([0, 1, 1023, 1024, 4095, 4096, 4097, 5120, 65535, 65536, 99999, 131071], dtype=np.int64)
+    ref = oracle.swa_prefill(f64(q), f64(k), f64(v), W, rows=rows)
+    got = out_f64(out)[:, rows]
+    ex = bf16_excess(got, ref)
+    assert ex <= 0, (ex, max_abs(got, ref))
+    held = oracle.ring_positions(L - 1, W)
+    assert np.array_equal(out_f64(rk)[0, :, 5], f64(k)[0, held[5]])
