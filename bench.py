@@ -12,6 +12,8 @@ One step is one pass over every operation of the path, each at its workload size
             each continuing from the ring the previous chunk left
   quant   kv_quant_int8_b32 K and V of batch 16, 63488 warm tokens, 8 kv heads
   int8    attn_decode_int8kv batch 16, context 65536 (2048 hot bf16 tokens), 32/8 heads
+  int8sparse  attn_decode_int8kv_sparse on the same pool: the hot tail plus each
+            head's top-64 32-token INT8 blocks (scored by q . block mean)
   sparse  blocksparse_select_attend  L 131072, 32/8 heads, 64-token blocks, top-64, window 1024
   hybrid70  one decode step of a 70-layer hybrid stack: 60 swa_decode_ring layers
             (window 128) and 10 full-attention layers (attn_decode_int8kv over an
@@ -117,6 +119,26 @@ def int8_decode_bytes(c=INT8) -> int:
     return codes + scales + hot + 2 * q
 
 
+def int8_sparse_bytes(sel, c=INT8) -> int:
+    """Bytes the block-sparse decode moves: per (sequence, KV head) the union of the
+    group's kept blocks (K and V codes + scales), the bf16 hot tail, the block
+    means read by the scoring, q and out."""
+    import numpy as np
+
+    B, Hq, topk = sel.shape
+    G = Hq // c["Hkv"]
+    nblk = (c["ctx"] - c["hot"]) // 32
+    blocks = 0
+    for b in range(B):
+        for g in range(c["Hkv"]):
+            s = sel[b, g * G:(g + 1) * G].ravel()
+            blocks += len(np.unique(s[s >= 0]))
+    per_block = 2 * (32 * c["D"] + 4)
+    hot = 2 * B * c["Hkv"] * c["hot"] * c["D"] * 2
+    means = B * c["Hkv"] * c["D"] * nblk * 4
+    return blocks * per_block + hot + means + 2 * B * Hq * c["D"] * 2
+
+
 def int8_quant_bytes(c=INT8) -> int:
     n = 2 * c["B"] * c["Hkv"] * (c["ctx"] - c["hot"]) * c["D"]
     return n * 2 + n + (n // (32 * c["D"])) * 4
@@ -219,7 +241,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--rows", default="ring,swa,full,chunk4096,chunk8192,quant,int8,sparse,hybrid70")
+    ap.add_argument("--rows", default="ring,swa,full,chunk4096,chunk8192,quant,int8,int8sparse,sparse,hybrid70")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -298,7 +320,7 @@ def main() -> int:
                         hsk.swa_prefill_chunk(cq[:, p0:p0 + C], ck[:, p0:p0 + C], cv[:, p0:p0 + C], rk, rv, p0,
                                               out=outs[i])
                 work[name] = chunk_run
-    if "quant" in rows or "int8" in rows:
+    if any(r in rows for r in ("quant", "int8", "int8sparse")):
         c = INT8
         t8 = c["ctx"] - c["hot"]
         kx = synth.normal_gpu(4, synth.K, (c["B"], c["Hkv"], c["ctx"], c["D"]), outlier_p=0.01)
@@ -323,6 +345,14 @@ def main() -> int:
             work["quant"] = quant_step
         if "int8" in rows:
             work["int8"] = lambda: hsk.attn_decode_int8kv(iq, kc, ks, vc, vs, khot, vhot, out=iout, workspace=iws)
+        if "int8sparse" in rows:
+            # the same pool decoded block-sparsely: hot tail + each head's top-64 INT8 blocks
+            kmeans = hsk.kv_block_means_int8(kc, ks)
+            isel = torch.empty((c["B"], c["Hq"], 64), dtype=torch.int32, device=dev)
+            isws = torch.empty(hsk.attn_decode_int8kv_sparse_workspace_size(c["B"], c["Hq"], c["Hkv"], c["D"], t8,
+                                                                           c["hot"], 64), dtype=torch.uint8, device=dev)
+            work["int8sparse"] = lambda: hsk.attn_decode_int8kv_sparse(iq, kc, ks, vc, vs, kmeans, khot, vhot, topk=64,
+                                                                       out=iout, sel=isel, workspace=isws)
     if "sparse" in rows:
         c = SPARSE
         sq = synth.normal_gpu(5, synth.Q, (c["L"], c["Hq"], c["D"]))
@@ -456,6 +486,13 @@ def main() -> int:
         gbs = int8_decode_bytes() / (ms * 1e-3) / 1e9
         res["int8"] = {"ms": round(ms, 4), "bytes": int8_decode_bytes(), "GB/s": round(gbs, 1),
                        "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    if "int8sparse" in rows:
+        ms = timer.mean_ms("int8sparse", args.warmup)
+        nb = int8_sparse_bytes(isel.cpu().numpy())
+        gbs = nb / (ms * 1e-3) / 1e9
+        res["int8sparse"] = {"ms": round(ms, 4), "topk_blocks": 64, "bytes": nb, "GB/s": round(gbs, 1),
+                             "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                             "vs_dense_bytes": round(nb / int8_decode_bytes(), 4)}
     if "sparse" in rows:
         c = SPARSE
         ms = timer.mean_ms("sparse", args.warmup)

@@ -9,6 +9,9 @@ raises if it is missing.
 from .api import (  # noqa: F401
     attn_decode_int8kv,
     attn_decode_int8kv_workspace_size,
+    attn_decode_int8kv_sparse,
+    attn_decode_int8kv_sparse_workspace_size,
+    kv_block_means_int8,
     blocksparse_select_attend,
     blocksparse_workspace_size,
     kv_quant_int8_b32,

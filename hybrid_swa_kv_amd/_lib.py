@@ -20,6 +20,9 @@ EXPORTS = (
     "blocksparse_workspace_size",
     "swa_window_safe_len",
     "swa_prefill_chunk",
+    "kv_block_means_int8",
+    "attn_decode_int8kv_sparse",
+    "attn_decode_int8kv_sparse_workspace_size",
 )
 
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -36,6 +39,10 @@ _SIGS = {
     "blocksparse_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "swa_window_safe_len": (_I, [_P, _P, _P, _I, _I, _P]),
     "swa_prefill_chunk": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "kv_block_means_int8": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    "attn_decode_int8kv_sparse": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+                                       _P, _S, _P]),
+    "attn_decode_int8kv_sparse_workspace_size": (_S, [_I, _I, _I, _I, _I, _I, _I]),
 }
 
 _lib = None

@@ -228,3 +228,52 @@ def swa_prefill_chunk(q, k, v, ring_k, ring_v, pos0: int, scale: float | None = 
     _check(_lib.load().swa_prefill_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ring_k), _ptr(ring_v),
                                          B, C, Hq, Hkv, D, W, int(pos0), scale, _stream(stream)))
     return out
+
+
+def kv_block_means_int8(codes, scales, means=None, stream=None):
+    """K block means of INT8 codes [B, Hkv, T8, D] with scales [B, Hkv, T8/32].
+
+    Returns means float32 [B, Hkv, D, T8/32] (d-major).
+    """
+    _need(codes, "codes", torch.int8, 4)
+    _need(scales, "scales", torch.float32, 3)
+    B, Hkv, T8, D = codes.shape
+    means = _out(means, "means", torch.float32, (B, Hkv, D, T8 // 32), codes.device)
+    _check(_lib.load().kv_block_means_int8(_ptr(codes), _ptr(scales), _ptr(means), B, Hkv, T8, D,
+                                           _stream(stream)))
+    return means
+
+
+def attn_decode_int8kv_sparse_workspace_size(B, Hq, Hkv, D, T8, Th, topk) -> int:
+    return int(_lib.load().attn_decode_int8kv_sparse_workspace_size(B, Hq, Hkv, D, T8, Th, topk))
+
+
+def attn_decode_int8kv_sparse(q, k_codes, k_scales, v_codes, v_scales, k_means, k_hot, v_hot, topk: int = 64,
+                              scale: float | None = None, out=None, sel=None, workspace=None, stream=None):
+    """Decode over the bf16 hot tail and each head's top-k INT8 blocks (by q . block mean).
+
+    Returns (out [B, Hq, D] bf16, sel [B, Hq, topk] int32).
+    """
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_hot, "k_hot", torch.bfloat16, 4)
+    _need(v_hot, "v_hot", torch.bfloat16, 4)
+    B, Hq, D = q.shape
+    Hkv, Th = k_hot.shape[1], k_hot.shape[2]
+    T8 = 0 if k_codes is None else k_codes.shape[2]
+    if T8:
+        _need(k_codes, "k_codes", torch.int8, 4)
+        _need(v_codes, "v_codes", torch.int8, 4)
+        _need(k_scales, "k_scales", torch.float32, 3)
+        _need(v_scales, "v_scales", torch.float32, 3)
+        _need(k_means, "k_means", torch.float32, 4)
+    out = _out(out, "out", torch.bfloat16, q.shape, q.device)
+    sel = _out(sel, "sel", torch.int32, (B, Hq, topk), q.device)
+    need = attn_decode_int8kv_sparse_workspace_size(B, Hq, Hkv, D, T8, Th, topk)
+    workspace = _scratch(workspace, "workspace", need, q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    opt = (lambda t: _ptr(t) if T8 else None)
+    _check(_lib.load().attn_decode_int8kv_sparse(
+        _ptr(q), opt(k_codes), opt(k_scales), opt(v_codes), opt(v_scales), opt(k_means), _ptr(k_hot), _ptr(v_hot),
+        _ptr(out), _ptr(sel) if topk > 0 else None, B, Hq, Hkv, D, T8, Th, topk, scale, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, sel

@@ -2,6 +2,7 @@
 // Nothing here allocates device memory or keeps state between calls.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -10,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;  // 2: swa_window_safe_len, 3: swa_prefill_chunk
+constexpr int kAbiVersion = 4;  // 2: swa_window_safe_len, 3: swa_prefill_chunk, 4: sparse INT8 decode
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -37,6 +38,35 @@ size_t bs_ws_bytes(int L, int Hq, int Hkv, int D, int block) {
   const size_t nb = (size_t)L / block;
   const size_t nbp = (nb + 63) / 64 * 64;
   return (((size_t)Hq + Hkv) * nbp * D + (size_t)Hq * (nb * (nb - 1) / 2)) * sizeof(double);
+}
+
+// Block-sparse INT8 decode plan and workspace: fp64 scores [B, Hq, nblk], the
+// per-unit union list and head bits [units, lmax], counts [units], then the
+// split records [units, nss + nsh, G, D + 2] fp32 (segments 256-byte aligned).
+struct SparsePlan {
+  int nblk, lmax, epsplit, nss, hsplit, nsh;
+  size_t off_scores, off_list, off_mask, off_count, off_rec, bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+SparsePlan sparse_plan(int B, int Hq, int Hkv, int D, int T8, int Th, int topk) {
+  SparsePlan p{};
+  const int G = Hq / Hkv;
+  const size_t units = (size_t)B * Hkv;
+  p.nblk = T8 / 32;
+  p.lmax = topk > 0 ? std::min(p.nblk, G * topk) : 0;
+  p.epsplit = 32;
+  p.nss = (p.lmax + p.epsplit - 1) / p.epsplit;
+  p.hsplit = 512;
+  p.nsh = (Th + p.hsplit - 1) / p.hsplit;
+  p.off_scores = 0;
+  p.off_list = align256(p.off_scores + (size_t)B * Hq * p.nblk * sizeof(double));
+  p.off_mask = align256(p.off_list + units * p.lmax * sizeof(int32_t));
+  p.off_count = align256(p.off_mask + units * p.lmax * sizeof(uint32_t));
+  p.off_rec = align256(p.off_count + units * sizeof(int32_t));
+  p.bytes = p.off_rec + units * (size_t)(p.nss + p.nsh) * G * (D + 2) * sizeof(float);
+  return p;
 }
 
 }  // namespace
@@ -258,6 +288,68 @@ int swa_window_safe_len(const int32_t* slot_pos, const int32_t* match_len, int32
   a.B = B;
   a.W = W;
   return finish(hsk::launch_window_safe(a, (hipStream_t)stream));
+}
+
+int kv_block_means_int8(const int8_t* codes, const float* scales, float* means, int B, int Hkv, int T8, int D,
+                        void* stream) {
+  if (B <= 0 || Hkv <= 0 || T8 < 0 || T8 % 32 != 0) return HSK_ERR_SHAPE;
+  if (!head_dim_ok(D)) return HSK_ERR_UNSUPPORTED;
+  if (T8 == 0) return HSK_OK;
+  if (!codes || !scales || !means) return HSK_ERR_NULL;
+  if (!aligned4(scales) || !aligned4(means)) return HSK_ERR_ALIGN;
+  hsk::BlockMeansArgs a{};
+  a.codes = codes; a.scales = scales; a.means = means;
+  a.units = B * Hkv; a.T8 = T8; a.D = D;
+  return finish(hsk::launch_block_means(a, (hipStream_t)stream));
+}
+
+size_t attn_decode_int8kv_sparse_workspace_size(int B, int Hq, int Hkv, int D, int T8, int Th, int topk) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || T8 < 0 || Th <= 0 || topk < 0) return 0;
+  return sparse_plan(B, Hq, Hkv, D, T8, Th, topk).bytes;
+}
+
+int attn_decode_int8kv_sparse(const void* q, const int8_t* k_codes, const float* k_scales, const int8_t* v_codes,
+                              const float* v_scales, const float* k_means, const void* k_hot, const void* v_hot,
+                              void* out, int32_t* sel, int B, int Hq, int Hkv, int D, int T8, int Th, int topk,
+                              float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_hot || !v_hot || !out) return HSK_ERR_NULL;
+  if (topk > 0 && !sel) return HSK_ERR_NULL;
+  if (T8 > 0 && (!k_codes || !k_scales || !v_codes || !v_scales || !k_means)) return HSK_ERR_NULL;
+  if (B <= 0 || T8 < 0 || T8 % 32 != 0 || Th <= 0 || topk < 0) return HSK_ERR_SHAPE;
+  if (int rc = check_heads(Hq, Hkv, D)) return rc;
+  if (Hq / Hkv > 16 || topk > 256 || T8 / 32 > 4096) return HSK_ERR_UNSUPPORTED;
+  if ((long long)T8 * D >= (1ll << 31)) return HSK_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return HSK_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_hot) || !aligned16(v_hot) || !aligned16(out) || (sel && !aligned4(sel)))
+    return HSK_ERR_ALIGN;
+  if (T8 > 0 && (!aligned16(k_codes) || !aligned16(v_codes) || !aligned4(k_scales) || !aligned4(v_scales) ||
+                 !aligned4(k_means)))
+    return HSK_ERR_ALIGN;
+  const SparsePlan p = sparse_plan(B, Hq, Hkv, D, T8, Th, topk);
+  if (!workspace || workspace_bytes < p.bytes) return HSK_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return HSK_ERR_ALIGN;
+  char* ws = (char*)workspace;
+  hsk::SparseDecodeArgs a{};
+  a.q = (const uint16_t*)q;
+  a.kc = k_codes; a.ks = k_scales; a.vc = v_codes; a.vs = v_scales; a.means = k_means;
+  a.kh = (const uint16_t*)k_hot; a.vh = (const uint16_t*)v_hot;
+  a.out = (uint16_t*)out;
+  a.sel = sel;
+  a.scores = (double*)(ws + p.off_scores);
+  a.ulist = (int32_t*)(ws + p.off_list);
+  a.umask = (uint32_t*)(ws + p.off_mask);
+  a.ucount = (int32_t*)(ws + p.off_count);
+  a.ws = (float*)(ws + p.off_rec);
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T8 = T8; a.Th = Th; a.topk = topk;
+  a.nblk = p.nblk; a.lmax = p.lmax;
+  a.epsplit = p.epsplit; a.nss = p.nss; a.hsplit = p.hsplit; a.nsh = p.nsh;
+  a.scale_log2 = log2e_times(scale);
+  hipStream_t s = (hipStream_t)stream;
+  if (topk > 0) {
+    const hipError_t e = hsk::launch_sparse_select(a, s);
+    if (e != hipSuccess) return HSK_ERR_HIP;
+  }
+  return finish(hsk::launch_sparse_decode(a, s));
 }
 
 }  // extern "C"

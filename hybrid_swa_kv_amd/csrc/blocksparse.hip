@@ -26,6 +26,7 @@
 #include "common.hpp"
 #include "flash_tile.hpp"
 #include "kernels.hpp"
+#include "topk.hpp"
 
 namespace hsk {
 
@@ -63,10 +64,6 @@ __global__ __launch_bounds__(SUM_THREADS) void bs_sums_kernel(BlockSparseArgs a)
   }
 }
 
-__device__ __forceinline__ unsigned long long order_key(double x) {
-  const unsigned long long u = (unsigned long long)__double_as_longlong(x + 0.0);  // -0 -> +0
-  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-}
 
 // row qb of head h in the packed score triangle (key blocks 0 .. qb-1)
 __device__ __forceinline__ size_t tri_row(const BlockSparseArgs& a, int h, int qb) {
@@ -157,68 +154,7 @@ __global__ __launch_bounds__(256) void bs_select_kernel(BlockSparseArgs a) {
     const int kb = i * 64 + lane;
     keys[i] = (i < ngr && kb < n) ? order_key(row[kb]) : 0ull;  // 0 sorts below every key
   }
-  auto count_ge = [&](unsigned long long c) {
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < MAXG; ++i)
-      if (i < ngr) cnt += __popcll(__ballot(keys[i] >= c));
-    return cnt;
-  };
-  // 1. the top 16 bits over every candidate
-  unsigned long long T = 0;
-  for (int bit = 63; bit >= 48; --bit) {
-    const unsigned long long cand = T | (1ull << bit);
-    if (count_ge(cand) >= topk) T = cand;
-  }
-  // 2. the low 48 bits: only keys with T's 16-bit prefix can still change a count
-  const unsigned long long pre = T >> 48;
-  const int above = pre == 0xffffull ? 0 : count_ge((pre + 1) << 48);
-  const unsigned long long lt_mask = (1ull << lane) - 1ull;
-  int neq = 0;
-#pragma unroll
-  for (int i = 0; i < MAXG; ++i) {
-    if (i >= ngr) continue;
-    const bool eq = (keys[i] >> 48) == pre && keys[i] != 0ull;
-    const unsigned long long m = __ballot(eq);
-    const int pos = neq + __popcll(m & lt_mask);
-    if (eq && pos < 64) gather[w][pos] = keys[i];
-    neq += __popcll(m);
-  }
-  if (neq <= 64) {
-    __builtin_amdgcn_wave_barrier();
-    const unsigned long long ek = lane < neq ? gather[w][lane] : 0ull;
-    for (int bit = 47; bit >= 0; --bit) {
-      const unsigned long long cand = T | (1ull << bit);
-      if (above + (int)__popcll(__ballot(ek >= cand)) >= topk) T = cand;
-    }
-  } else {  // many candidates share the prefix (ties): search over all of them
-    for (int bit = 47; bit >= 0; --bit) {
-      const unsigned long long cand = T | (1ull << bit);
-      if (count_ge(cand) >= topk) T = cand;
-    }
-  }
-  int gt = 0;
-#pragma unroll
-  for (int i = 0; i < MAXG; ++i)
-    if (i < ngr) gt += __popcll(__ballot(keys[i] > T));
-  const int need = topk - gt;
-  int eq_before = 0, written = 0;
-#pragma unroll
-  for (int i = 0; i < MAXG; ++i) {
-    if (i >= ngr) continue;
-    const int kb = i * 64 + lane;
-    const bool valid = kb < n;
-    const bool is_gt = valid && keys[i] > T;
-    const bool is_eq = valid && keys[i] == T;
-    const unsigned long long eqb = __ballot(is_eq);
-    const int rank = eq_before + __popcll(eqb & lt_mask);
-    const bool take = is_gt || (is_eq && rank < need);
-    const unsigned long long tb = __ballot(take);
-    const int slot = written + __popcll(tb & lt_mask);
-    if (take && slot < topk) out[slot] = kb;
-    written += __popcll(tb);
-    eq_before += __popcll(eqb);
-  }
+  const int written = topk_select_row<MAXG>(keys, ngr, n, topk, gather[w], [&](int slot, int kb) { out[slot] = kb; });
   for (int i = written + lane; i < topk; i += 64) out[i] = -1;
 }
 

@@ -99,6 +99,90 @@ __global__ __launch_bounds__(DQ_THREADS) void int8_decode_kernel(Int8DecodeArgs 
   }
 }
 
+// Block-sparse variant: the INT8 splits walk the union of blocks kept by the
+// group's heads (written by the selection) instead of a token range; each chunk
+// is one kept block, and heads that did not keep it have its scores masked.  A
+// wave's list entries are read once into lanes and broadcast per step.  Hot
+// splits and split records are as above.
+template <int D>
+__global__ __launch_bounds__(DQ_THREADS) void int8_sparse_decode_kernel(SparseDecodeArgs a) {
+  __shared__ float sm_m[4][16], sm_l[4][16];
+  __shared__ float sm_o[4][16][D + 1];
+
+  const int nsplit = a.nss + a.nsh;
+  const int nhot = a.B * a.Hkv * a.nsh;
+  const int i = blockIdx.x;
+  const int unit = i < nhot ? i / a.nsh : (i - nhot) / a.nss;
+  const int split = i < nhot ? a.nss + i % a.nsh : (i - nhot) % a.nss;
+  const int g = unit % a.Hkv, b = unit / a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = __lane_id();
+
+  DecodeWave<D> st;
+  st.init(a.q + ((size_t)b * a.Hq + g * G) * D, G);
+
+  if (split < a.nss) {
+    const int cnt = a.ucount[unit];
+    const int e0 = split * a.epsplit, e1 = min(cnt, e0 + a.epsplit);
+    const int nmine = e1 > e0 + w ? (e1 - e0 - w + 3) / 4 : 0;  // entries e0 + w + 4 k
+    int myblk = 0;
+    unsigned mymask = 0u;
+    if (lane < nmine) {
+      myblk = a.ulist[(size_t)unit * a.lmax + e0 + w + 4 * lane];
+      mymask = a.umask[(size_t)unit * a.lmax + e0 + w + 4 * lane];
+    }
+    const int8_t* kc = a.kc + (size_t)unit * a.T8 * D;
+    const int8_t* vc = a.vc + (size_t)unit * a.T8 * D;
+    const int nbytes = a.T8 * D;
+    const Int8Rows<D> rows{kc, vc, __builtin_amdgcn_make_buffer_rsrc((void*)kc, (short)0, nbytes, 0x00020000),
+                           __builtin_amdgcn_make_buffer_rsrc((void*)vc, (short)0, nbytes, 0x00020000)};
+    const float* ks = a.ks + (size_t)unit * a.nblk;
+    const float* vs = a.vs + (size_t)unit * a.nblk;
+    using Raw = typename DecodeWave<D>::template Raw<true>;
+    auto blk = [&](int k) { return __builtin_amdgcn_readlane(myblk, k); };
+    auto step = [&](int k, Raw& cur, Raw& ahead) {
+      if (k + 2 < nmine) st.template load<true>(rows, 32 * blk(k + 2), ahead);
+      const int j = blk(k);
+      st.template compute<true>(rows, 32 * j, cur, ks[j] * a.scale_log2, vs[j],
+                                (unsigned)__builtin_amdgcn_readlane((int)mymask, k));
+    };
+    if (nmine > 0) {  // three blocks in flight, as in the dense decode
+      Raw r0, r1, r2;
+      st.template load<true>(rows, 32 * blk(0), r0);
+      if (nmine > 1) st.template load<true>(rows, 32 * blk(1), r1);
+      for (int k = 0;; k += 3) {
+        step(k, r0, r2);
+        if (k + 1 >= nmine) break;
+        step(k + 1, r1, r0);
+        if (k + 2 >= nmine) break;
+        step(k + 2, r2, r1);
+        if (k + 3 >= nmine) break;
+      }
+    }
+  } else {
+    const int tok0 = (split - a.nss) * a.hsplit;
+    const int tok1 = min(a.Th, tok0 + a.hsplit);
+    const Bf16Rows<D> rows{a.kh + (size_t)unit * a.Th * D, a.vh + (size_t)unit * a.Th * D, tok1};
+    for (int c0 = tok0 + 32 * w; c0 < tok1; c0 += 128) st.template chunk<false>(rows, c0, a.scale_log2, 1.f);
+  }
+
+  st.stash(sm_m, sm_l, sm_o, w, G);
+  __syncthreads();
+  float* rec0 = a.ws + ((size_t)unit * nsplit + split) * G * (D + 2);
+  for (int e = threadIdx.x; e < G * D; e += DQ_THREADS) {
+    const int head = e / D, d = e % D;
+    float M, Ls;
+    const float O = merge_waves<4, D>(sm_m, sm_l, sm_o, head, d, M, Ls);
+    float* rec = rec0 + (size_t)head * (D + 2);
+    rec[d] = O;
+    if (d == 0) {
+      rec[D] = M;
+      rec[D + 1] = Ls;
+    }
+  }
+}
+
 // merge split records in split order: out = sum 2^(m_i - M) acc_i / sum 2^(m_i - M) l_i
 // One workgroup per (sequence, query head); split weights go through LDS so the
 // per-d loop issues independent loads.
@@ -177,6 +261,22 @@ hipError_t launch_int8_decode(const Int8DecodeArgs& a, hipStream_t s) {
   } else {
     hipLaunchKernelGGL(int8_decode_kernel<64>, dim3(grid), dim3(DQ_THREADS), 0, s, a);
     hipLaunchKernelGGL(int8_combine_kernel<64>, dim3(a.B * a.Hq), dim3(64), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_decode(const SparseDecodeArgs& a, hipStream_t s) {
+  const int grid = a.B * a.Hkv * (a.nss + a.nsh);
+  Int8DecodeArgs c{};  // the combine reads only these fields
+  c.out = a.out; c.ws = a.ws;
+  c.B = a.B; c.Hq = a.Hq; c.Hkv = a.Hkv; c.D = a.D;
+  c.ns8 = a.nss; c.nsh = a.nsh;
+  if (a.D == 128) {
+    hipLaunchKernelGGL(int8_sparse_decode_kernel<128>, dim3(grid), dim3(DQ_THREADS), 0, s, a);
+    hipLaunchKernelGGL(int8_combine_kernel<128>, dim3(a.B * a.Hq), dim3(128), 0, s, c);
+  } else {
+    hipLaunchKernelGGL(int8_sparse_decode_kernel<64>, dim3(grid), dim3(DQ_THREADS), 0, s, a);
+    hipLaunchKernelGGL(int8_combine_kernel<64>, dim3(a.B * a.Hq), dim3(64), 0, s, c);
   }
   return hipGetLastError();
 }

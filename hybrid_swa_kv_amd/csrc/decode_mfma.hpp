@@ -180,16 +180,19 @@ struct DecodeWave {
       }
   }
 
+  // head_bits: bit hl set when head hl takes part in this chunk (a block-sparse
+  // decode keeps different blocks per head); the other heads' scores are masked.
   template <bool INT8, int NT = 2, class Rows>
-  __device__ __forceinline__ void compute(const Rows& rows, int c0, Raw<INT8>& raw, float sk, float sv) {
+  __device__ __forceinline__ void compute(const Rows& rows, int c0, Raw<INT8>& raw, float sk, float sv,
+                                          unsigned head_bits = ~0u) {
     AltRow none;
-    compute<INT8, NT>(rows, c0, raw, sk, sv, none);
+    compute<INT8, NT>(rows, c0, raw, sk, sv, none, head_bits);
   }
 
   // alt: the replacing row (used when Rows::kHasAlt and it falls in this chunk)
   template <bool INT8, int NT = 2, class Rows>
   __device__ __forceinline__ void compute(const Rows& rows, int c0, Raw<INT8>& raw, float sk, float sv,
-                                          const AltRow& alt) {
+                                          const AltRow& alt, unsigned head_bits = ~0u) {
     const int lane = __lane_id();
     const int hl = lane & 15, gq = lane >> 4;
     constexpr int KV = Raw<INT8>::KV;
@@ -297,6 +300,7 @@ struct DecodeWave {
         if (t < NT) {
           v = s[t][r] * sk;
           if (partial && !rows.valid(c0 + 16 * t + 4 * gq + r)) v = kNegInf;
+          if (!((head_bits >> hl) & 1u)) v = kNegInf;
         }
         x[4 * t + r] = v;
         mx = fmaxf(mx, v);

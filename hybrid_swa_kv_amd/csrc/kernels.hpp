@@ -93,6 +93,38 @@ struct WindowSafeArgs {
   int B, W;
 };
 
+struct BlockMeansArgs {
+  const int8_t* codes;  // [B, Hkv, T8, D]
+  const float* scales;  // [B, Hkv, T8/32]
+  float* means;         // [B, Hkv, D, T8/32] (d-major)
+  int units, T8, D;     // units = B * Hkv
+};
+
+// Block-sparse decode over the hot + INT8 pool.  Per (sequence, KV head) unit the
+// selection writes the union of the group's kept blocks, ascending, with a bit
+// per head that kept each block.
+struct SparseDecodeArgs {
+  const uint16_t* q;     // [B, Hq, D]
+  const int8_t* kc;      // [B, Hkv, T8, D]
+  const float* ks;       // [B, Hkv, T8/32]
+  const int8_t* vc;
+  const float* vs;
+  const float* means;    // [B, Hkv, D, T8/32] K block means
+  const uint16_t* kh;    // [B, Hkv, Th, D]
+  const uint16_t* vh;
+  uint16_t* out;         // [B, Hq, D]
+  int32_t* sel;          // [B, Hq, topk]
+  int32_t* ulist;        // [units, lmax] kept blocks of the group, ascending
+  uint32_t* umask;       // [units, lmax] bit per head of the group
+  int32_t* ucount;       // [units]
+  double* scores;        // [B, Hq, nblk] block scores
+  float* ws;             // split records, as the dense decode
+  int B, Hq, Hkv, D, T8, Th, topk, nblk, lmax;
+  int epsplit, nss;      // union entries per sparse split, sparse splits per unit
+  int hsplit, nsh;       // hot tokens per hot split, hot splits per unit
+  float scale_log2;
+};
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_ring(const RingCopyArgs& a, hipStream_t s);
@@ -102,5 +134,8 @@ void int8_decode_plan(int B, int Hkv, int T8, int Th, int* split8, int* splith, 
 hipError_t launch_int8_decode(const Int8DecodeArgs& a, hipStream_t s);
 hipError_t launch_blocksparse(const BlockSparseArgs& a, hipStream_t s);
 hipError_t launch_window_safe(const WindowSafeArgs& a, hipStream_t s);
+hipError_t launch_block_means(const BlockMeansArgs& a, hipStream_t s);
+hipError_t launch_sparse_select(const SparseDecodeArgs& a, hipStream_t s);  // scores, then selection
+hipError_t launch_sparse_decode(const SparseDecodeArgs& a, hipStream_t s);
 
 }  // namespace hsk

@@ -174,6 +174,49 @@ int attn_decode_int8kv(const void* q,
 size_t attn_decode_int8kv_workspace_size(int B, int Hq, int Hkv, int D, int T8, int Th);
 
 /*
+ * kv_block_means_int8 — the K block means stored with the INT8 blocks.
+ *
+ * For the block-sparse decode below ([K25-arch] section 2.2: a query keeps its
+ * top-64 long-range keys; section 2.3: 32-token INT8 blocks): per (sequence,
+ * KV head, 32-token block) and d, mean = fl32(fl32(sum of the 32 codes) * scale)
+ * / 32 -- the code sum is an exact integer, so one fp32 rounding; the division
+ * by 32 is exact (bit-exact output).
+ *
+ * codes  [B, Hkv, T8, D] int8;  scales [B, Hkv, T8/32] fp32
+ * means  [B, Hkv, D, T8/32] fp32, written (d-major)
+ * Errors: HSK_ERR_SHAPE unless T8 % 32 == 0; T8 == 0 is a no-op.
+ */
+int kv_block_means_int8(const int8_t* codes, const float* scales, float* means,
+                        int B, int Hkv, int T8, int D, void* stream);
+
+/*
+ * attn_decode_int8kv_sparse — top-k block-sparse decode over the hot + INT8 pool.
+ *
+ * [K25-arch] section 2.2 joins the hot/warm KV ("direction one") with a local
+ * window plus top-64 long-range attention ("direction two").  Here the local
+ * window is the bf16 hot tail (always attended) and the long-range candidates
+ * are the 32-token INT8 blocks: per query head, score(j) = q . mean_j in fp64
+ * (means from kv_block_means_int8); the topk highest are kept, ties to the lower
+ * block, all blocks when there are at most topk.  The query (position T8+Th-1)
+ * attends the hot tail and the tokens of its kept blocks.
+ *
+ * q [B, Hq, D] bf16; codes/scales as attn_decode_int8kv; k_means [B, Hkv, D, T8/32]
+ * fp32; k_hot, v_hot [B, Hkv, Th, D] bf16; out [B, Hq, D] bf16, written;
+ * sel [B, Hq, topk] int32, written: kept blocks ascending, -1 padded (bit-exact
+ * up to fp64 near-ties).  workspace: attn_decode_int8kv_sparse_workspace_size(...).
+ * Limits: Hq / Hkv <= 16, topk <= 256, T8 / 32 <= 4096, T8 * D < 2^31.
+ */
+int attn_decode_int8kv_sparse(const void* q,
+                              const int8_t* k_codes, const float* k_scales,
+                              const int8_t* v_codes, const float* v_scales,
+                              const float* k_means, const void* k_hot, const void* v_hot,
+                              void* out, int32_t* sel,
+                              int B, int Hq, int Hkv, int D, int T8, int Th, int topk, float scale,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+size_t attn_decode_int8kv_sparse_workspace_size(int B, int Hq, int Hkv, int D, int T8, int Th, int topk);
+
+/*
  * blocksparse_select_attend — top-k block-sparse causal attention.
  *
  * [K25-arch] section 2.2 "direction two": a local sliding window plus sparse

@@ -37,6 +37,7 @@ from .attention import (  # noqa: F401
 from .ring import ring_slot, ring_fill, ring_append, ring_positions  # noqa: F401
 from .prefix import window_safe_len  # noqa: F401
 from .chunk import swa_prefill_chunk  # noqa: F401
+from .sparse_decode import int8_block_means, sparse_select, attn_decode_int8kv_sparse  # noqa: F401
 from .quant import kv_quant_int8_b32, dequant_int8_b32  # noqa: F401
 from .select import block_sums, block_scores, block_select  # noqa: F401
 from .closed_forms import (  # noqa: F401

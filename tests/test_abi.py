@@ -142,3 +142,22 @@ def test_prefill_chunk_validation(lib):
     assert f(P, P, P, P, P, P, 1, 64, 8, 2, 96, 128, 0, 1.0, None) == UNSUP      # head_dim
     assert f(P, P, P, P, P, P, 1, 64, 8, 2, 128, 128, 0, 0.0, None) == SHAPE
     assert f(P, P, P, MIS, P, P, 1, 64, 8, 2, 128, 128, 0, 1.0, None) == ALIGN
+
+
+def test_sparse_decode_validation(lib):
+    f = lib.attn_decode_int8kv_sparse
+    need = lib.attn_decode_int8kv_sparse_workspace_size(16, 32, 8, 128, 63488, 2048, 64)
+    assert need > 0
+    assert lib.attn_decode_int8kv_sparse_workspace_size(16, 32, 8, 128, 63488, 2048, -1) == 0
+    #        q  kc ks vc vs km kh vh out sel B  Hq Hkv D  T8  Th topk scale ws wsb stream
+    assert f(P, P, P, P, P, P, P, P, P, None, 2, 8, 2, 128, 64, 16, 4, 1.0, P, need, None) == NULL
+    assert f(P, P, P, P, P, None, P, P, P, P, 2, 8, 2, 128, 64, 16, 4, 1.0, P, need, None) == NULL
+    assert f(P, P, P, P, P, P, P, P, P, P, 2, 8, 2, 128, 48, 16, 4, 1.0, P, need, None) == SHAPE
+    assert f(P, P, P, P, P, P, P, P, P, P, 2, 8, 2, 128, 64, 16, 300, 1.0, P, need, None) == UNSUP
+    assert f(P, P, P, P, P, P, P, P, P, P, 2, 64, 2, 128, 64, 16, 4, 1.0, P, need, None) == UNSUP
+    assert f(P, P, P, P, P, P, P, P, P, P, 2, 8, 2, 128, 64, 16, 4, 1.0, P, 0, None) == WS
+    g = lib.kv_block_means_int8
+    assert g(P, P, P, 2, 2, 48, 128, None) == SHAPE
+    assert g(None, None, None, 2, 2, 0, 128, None) == 0
+    assert g(None, P, P, 2, 2, 64, 128, None) == NULL
+    assert g(P, P, P, 2, 2, 64, 96, None) == UNSUP
