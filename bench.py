@@ -362,8 +362,8 @@ def main() -> int:
         ssel = torch.empty((c["Hq"], c["L"] // c["block"], c["topk"]), dtype=torch.int32, device=dev)
         sws = torch.empty(hsk.blocksparse_workspace_size(c["L"], c["Hq"], c["Hkv"], c["D"], c["block"], c["topk"]),
                           dtype=torch.uint8, device=dev)
-        work["sparse"] = lambda: hsk.blocksparse_select_attend(sq, sk, sv, c["block"], c["topk"], c["W"],
-                                                               out=sout, sel=ssel, workspace=sws)
+        work["sparse"] = lambda c=c: hsk.blocksparse_select_attend(sq, sk, sv, c["block"], c["topk"], c["W"],
+                                                                   out=sout, sel=ssel, workspace=sws)
     if "hybrid70" in rows:
         c = HYBRID
         kinds = hybrid_layers()
