@@ -158,11 +158,26 @@ __global__ __launch_bounds__(256) void bs_select_kernel(BlockSparseArgs a) {
   for (int i = written + lane; i < topk; i += 64) out[i] = -1;
 }
 
+// Number of tile stages of the attend kernel; NST stages keep NST-1 tiles in
+// flight per workgroup.  Two stages (64 KB of LDS at D = 128) leave room for two
+// workgroups per CU; three or four stages keep more tiles in flight but fit one
+// workgroup per CU and measure about 1.7x slower.
+constexpr int NST = 2;
+
+// Stage s of the ring, one __shared__ object each: slices of a single array
+// would make the compiler wait for every outstanding tile DMA before each LDS
+// read, since it could not tell the stages apart.
+template <int D, int S>
+__device__ __forceinline__ char* bs_stage() {
+  __shared__ __attribute__((aligned(16))) char buf[2 * FtCfg<D>::TILE];
+  return buf;
+}
+
 // grid: Hq * nb
 template <int D>
 __global__ __launch_bounds__(AT_THREADS) void bs_attend_kernel(BlockSparseArgs a) {
   using C = FtCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * C::TILE];
+  static_assert(NST >= 2 && NST <= 4, "2 to 4 stages");
   __shared__ int list[256];                  // selected blocks before the window
   __shared__ unsigned selbits[SEL_MAXNB / 32];
   __shared__ int s_npre;
@@ -212,16 +227,33 @@ __global__ __launch_bounds__(AT_THREADS) void bs_attend_kernel(BlockSparseArgs a
 
   TileDma<D, AT_THREADS> dma;
   dma.init(a.k + (size_t)g * D, a.v + (size_t)g * D, (unsigned)(a.Hkv * D * 2), L, w);
-  auto tile_of = [&](int it) { return it < npre ? list[it] : kw0 + (it - npre); };
-  dma.issue(tile_of(0), smem);
-  for (int it = 0; it < ntiles; ++it) {
-    wait_vmem();
-    __syncthreads();
-    const int kt = tile_of(it);
-    if (it + 1 < ntiles) dma.issue(tile_of(it + 1), smem + ((it + 1) & 1) * 2 * C::TILE);
-    const char* ks = smem + (it & 1) * 2 * C::TILE;
-    const bool full = (selbits[kt >> 5] >> (kt & 31)) & 1u;
-    fw.tile(ks, ks + C::TILE, kt * FT_BN, r0, row, W, full, a.scale_log2);
+  // the tile index is uniform; saying so keeps the DMA offset scalar (an LDS value
+  // would otherwise count as per-lane and the DMA would loop over lanes)
+  auto tile_of = [&](int it) { return __builtin_amdgcn_readfirstlane(it < npre ? list[it] : kw0 + (it - npre)); };
+  char* const stage[4] = {bs_stage<D, 0>(), bs_stage<D, 1>(), bs_stage<D, 2>(), bs_stage<D, 3>()};
+#pragma unroll
+  for (int p = 0; p < NST - 1; ++p)
+    if (p < ntiles) dma.issue(tile_of(p), stage[p]);
+  constexpr int PER_TILE = 2 * TileDma<D, AT_THREADS>::PER_WAVE;  // DMA instructions per tile per wave
+  // unrolled by NST so that every stage address is a compile-time constant
+  for (int it0 = 0; it0 < ntiles; it0 += NST) {
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      const int it = it0 + j;
+      if (it < ntiles) {
+        // tile it has landed once at most the later tiles' DMAs are outstanding
+        const int later = min(ntiles - 1 - it, NST - 2);
+        if (NST >= 4 && later >= 2) wait_vmem_upto<2 * PER_TILE>();
+        else if (NST >= 3 && later >= 1) wait_vmem_upto<PER_TILE>();
+        else wait_vmem_upto<0>();
+        lds_barrier();  // ... for every wave; and tile it-1's stage is free
+        const int kt = tile_of(it);
+        if (it + NST - 1 < ntiles) dma.issue(tile_of(it + NST - 1), stage[(j + NST - 1) % NST]);
+        const char* ks = stage[j];
+        const bool full = (selbits[kt >> 5] >> (kt & 31)) & 1u;
+        fw.tile(ks, ks + C::TILE, kt * FT_BN, r0, row, W, full, a.scale_log2);
+      }
+    }
   }
   fw.store(a.out + ((size_t)row * a.Hq + h) * D);
 }

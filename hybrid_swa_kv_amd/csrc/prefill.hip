@@ -25,8 +25,11 @@ constexpr int PF_THREADS = 256;
 // tiles before pos0 are fetched from the ring (slot tile (position mod W) / 64),
 // later ones from the chunk's own K/V.  pos0 and W are multiples of 64, so no
 // tile straddles the two sources.
+// smem0 / smem1 are the two tile stages.  They must be distinct __shared__
+// objects: carved out of one array, the compiler cannot tell the next tile's DMA
+// from the current tile's reads and waits for that DMA before every V read.
 template <int D, bool CHUNK>
-__device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
+__device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem0, char* smem1) {
   using C = FtCfg<D>;
 
   // XCD-aware order: consecutive logical units share (b, kv head, query block)
@@ -78,7 +81,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
       dma.issue(kt, buf);
     }
   };
-  issue(kt0, smem);
+  issue(kt0, smem0);
 
   // unrolled by two so each buffer's LDS offsets are compile-time constants
   auto step = [&](int it, char* cur, char* nxt) {
@@ -90,23 +93,25 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
   };
   int it = 0;
   for (; it + 1 < ntiles; it += 2) {
-    step(it, smem, smem + 2 * C::TILE);
-    step(it + 1, smem + 2 * C::TILE, smem);
+    step(it, smem0, smem1);
+    step(it + 1, smem1, smem0);
   }
-  if (it < ntiles) step(it, smem, smem + 2 * C::TILE);
+  if (it < ntiles) step(it, smem0, smem1);
   fw.store(rrow < L ? a.o + ((size_t)(b * (size_t)L + rrow) * a.Hq + h) * D : nullptr);
 }
 
 template <int D>
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * FtCfg<D>::TILE];
-  prefill_body<D, false>(a, smem);
+  __shared__ __attribute__((aligned(16))) char smem0[2 * FtCfg<D>::TILE];
+  __shared__ __attribute__((aligned(16))) char smem1[2 * FtCfg<D>::TILE];
+  prefill_body<D, false>(a, smem0, smem1);
 }
 
 template <int D>
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_chunk_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * FtCfg<D>::TILE];
-  prefill_body<D, true>(a, smem);
+  __shared__ __attribute__((aligned(16))) char smem0[2 * FtCfg<D>::TILE];
+  __shared__ __attribute__((aligned(16))) char smem1[2 * FtCfg<D>::TILE];
+  prefill_body<D, true>(a, smem0, smem1);
 }
 
 // fp32: one thread per (b, row, head); exact fp32 arithmetic with expf.
