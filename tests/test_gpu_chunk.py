@@ -65,3 +65,19 @@ def test_chunked_prefill_131072_in_4096_chunks_sampled():
     assert ex <= 0, (ex, max_abs(got, ref))
     held = oracle.ring_positions(L - 1, W)
     assert np.array_equal(out_f64(rk)[0, :, 5], f64(k)[0, held[5]])
+
+
+def test_chunks_of_8192_rows_sampled():
+    """Chunks of 8192 rows with 64 query heads; rows around query block edges of
+    both chunks and the chunk boundary."""
+    L, C, W, Hq, Hkv, D = 16384, 8192, 1024, 64, 8, 128
+    announce("prefill_chunk_8192", L=L, C=C, W=W)
+    q, k, v, out, rk, rv = _run_chunks(890, 1, L, C, Hq, Hkv, D, W)
+    edges = np.arange(0, L, 128)
+    rnd = np.random.default_rng(5).integers(0, L, size=48)
+    rows = np.concatenate([edges[::3], edges[1::3] - 1, edges[2::3] + 127, [C - 1, C, C + 1, L - 1], rnd])
+    rows = np.unique(rows[(rows >= 0) & (rows < L)]).astype(np.int64)
+    ref = oracle.swa_prefill(f64(q), f64(k), f64(v), W, rows=rows)
+    got = out_f64(out)[:, rows]
+    ex = bf16_excess(got, ref)
+    assert ex <= 0, (ex, max_abs(got, ref))

@@ -58,6 +58,28 @@ def test_bf16_parity(L, Hq, Hkv, D, W):
     assert ex <= 0, (ex, max_abs(out_f64(out), ref))
 
 
+def _block_edge_rows(L, seed, extra=64):
+    edges = np.arange(0, L, 128)
+    rnd = np.random.default_rng(seed).integers(0, L, size=extra)
+    rows = np.concatenate([edges, edges - 1, edges + 31, edges + 127, [L - 2, L - 1], rnd])
+    return np.unique(rows[(rows >= 0) & (rows < L)]).astype(np.int64)
+
+
+@pytest.mark.parametrize("L,W", [(8190, 128), (8325, 1024)])
+def test_bf16_64_heads_block_edges(L, W):
+    """64 query heads (8 per KV head) over about 8K rows, as in the long-context
+    workloads; rows around every 128-row query block edge and the ragged end."""
+    Hq, Hkv, D = 64, 8, 128
+    announce("prefill_bf16_64_heads", L=L, Hq=Hq, W=W)
+    q, k, v = _case(40 + L, None, L, Hq, Hkv, D, "bf16")
+    out = hsk.swa_prefill(gpu_bf16(q), gpu_bf16(k), gpu_bf16(v), W)
+    rows = _block_edge_rows(L, L)
+    got = out_f64(out)[rows]
+    ref = oracle.swa_prefill(f64(q), f64(k), f64(v), W, rows=rows)
+    ex = bf16_excess(got, ref)
+    assert ex <= 0, (ex, max_abs(got, ref))
+
+
 def test_bf16_batch_and_ring_output():
     B, L, Hq, Hkv, D, W = 3, 300, 4, 2, 128, 96
     announce("prefill_bf16_batch_ring", B=B, L=L)
