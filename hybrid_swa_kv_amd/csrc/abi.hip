@@ -28,9 +28,9 @@ int check_heads(int Hq, int Hkv, int D) {
 }
 
 size_t int8_ws_bytes(int B, int Hq, int Hkv, int D, int T8, int Th) {
-  int split8, splith, ns8, nsh;
-  hsk::int8_decode_plan(B, Hkv, T8, Th, &split8, &splith, &ns8, &nsh);
-  return (size_t)B * Hkv * (size_t)(ns8 + nsh) * (size_t)(Hq / Hkv) * (size_t)(D + 2) * sizeof(float);
+  int nsplit, wsplit;
+  hsk::int8_decode_plan(B, Hkv, T8, Th, &nsplit, &wsplit);
+  return (size_t)B * Hkv * (size_t)nsplit * (size_t)(Hq / Hkv) * (size_t)(D + 2) * sizeof(float);
 }
 
 // block sums [Hq + Hkv][D][nbp] and the score triangle [Hq][nb (nb - 1) / 2], fp64
@@ -232,7 +232,7 @@ int attn_decode_int8kv(const void* q, const int8_t* k_codes, const float* k_scal
   a.ws = (float*)workspace;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T8 = T8; a.Th = Th;
   a.scale_log2 = log2e_times(scale);
-  hsk::int8_decode_plan(B, Hkv, T8, Th, &a.split8, &a.splith, &a.ns8, &a.nsh);
+  hsk::int8_decode_plan(B, Hkv, T8, Th, &a.nsplit, &a.wsplit);
   return finish(hsk::launch_int8_decode(a, (hipStream_t)stream));
 }
 

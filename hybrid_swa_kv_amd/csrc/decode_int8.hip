@@ -1,7 +1,11 @@
 // Full-attention decode over an INT8 block-quantised region plus a bf16 hot tail.
 //
 // Split-K: one workgroup (4 waves) per (sequence, KV head, key range); waves take
-// interleaved 32-token chunks (one quantisation block each).  Per chunk a wave
+// interleaved 32-token chunks (one quantisation block each).  The key ranges
+// carry equal bytes (an INT8 token's 256 code bytes count once, a bf16 hot
+// token's 512 bytes twice); the last range of a sequence runs on from the INT8
+// tokens into the hot ones, so the grid is a whole number of rounds of equal
+// workgroups.  Per chunk a wave
 // runs v_mfma_f32_16x16x32_bf16 with the 16 query heads of the group on the N
 // axis (unused heads are zero columns):
 //   S   = K * q^T      A = K rows (16 keys x 32 d),  B = q^T,  lane l <-> head l%16
@@ -22,29 +26,30 @@ namespace hsk {
 namespace {
 
 constexpr int DQ_THREADS = 256;
+constexpr int DQ_TARGET_WGS = 2048;  // workgroups of the dense INT8 decode in all
 
 template <int D>
-__global__ __launch_bounds__(DQ_THREADS) void int8_decode_kernel(Int8DecodeArgs a) {
+__global__ __launch_bounds__(DQ_THREADS, 3) void int8_decode_kernel(Int8DecodeArgs a) {
   __shared__ float sm_m[4][16], sm_l[4][16];
   __shared__ float sm_o[4][16][D + 1];
 
-  const int nsplit = a.ns8 + a.nsh;
-  // the bf16 tail splits (twice the bytes of an INT8 split) are dispatched first
-  // so none of them starts in the last round of workgroups
-  const int nhot = a.B * a.Hkv * a.nsh;
-  const int i = blockIdx.x;
-  const int unit = i < nhot ? i / a.nsh : (i - nhot) / a.ns8;  // b * Hkv + g
-  const int split = i < nhot ? a.ns8 + i % a.nsh : (i - nhot) % a.ns8;
+  const int nsplit = a.nsplit;
+  const int unit = blockIdx.x / nsplit;  // b * Hkv + g
+  const int split = blockIdx.x % nsplit;
   const int g = unit % a.Hkv, b = unit / a.Hkv;
+  // this split's weight range -> INT8 tokens [t0, t1) and hot tokens [h0, h1)
+  const int wt = a.T8 + 2 * a.Th;
+  const int w0 = split * a.wsplit, w1 = min(wt, w0 + a.wsplit);
+  const int t0 = min(w0, a.T8), t1 = min(w1, a.T8);
+  const int h0 = max(w0 - a.T8, 0) / 2, h1 = max(w1 - a.T8, 0) / 2;
   const int G = a.Hq / a.Hkv;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   DecodeWave<D> st;
   st.init(a.q + ((size_t)b * a.Hq + g * G) * D, G);
 
-  if (split < a.ns8) {
-    const int tok0 = split * a.split8;
-    const int tok1 = min(a.T8, tok0 + a.split8);
+  if (t0 < t1) {
+    const int tok0 = t0, tok1 = t1;
     const int8_t* kc = a.kc + (size_t)unit * a.T8 * D;
     const int8_t* vc = a.vc + (size_t)unit * a.T8 * D;
     const int nbytes = a.T8 * D;  // < 2^31: checked at the boundary
@@ -52,32 +57,30 @@ __global__ __launch_bounds__(DQ_THREADS) void int8_decode_kernel(Int8DecodeArgs 
                            __builtin_amdgcn_make_buffer_rsrc((void*)vc, (short)0, nbytes, 0x00020000)};
     const float* ks = a.ks + (size_t)unit * (a.T8 / 32);
     const float* vs = a.vs + (size_t)unit * (a.T8 / 32);
-    // three chunks in flight per wave: the loads of chunk i+2 are issued before
-    // chunk i's math (unrolled by three, so the register images rotate instead of
-    // being copied).  HBM latency under full load is several microseconds, so the
-    // lookahead, not the math, sets the rate.
+    // two chunks in flight per wave: the loads of chunk i+1 are issued before
+    // chunk i's math (unrolled by two, so the register images alternate instead
+    // of being copied).  Two images keep the kernel within 168 VGPRs, three
+    // waves per SIMD; a third image in flight measured slower, since it halves
+    // the waves that hide the chunk math's latency.
     using Raw = typename DecodeWave<D>::template Raw<true>;
     auto step = [&](int c, Raw& cur, Raw& ahead) {
-      if (c + 256 < tok1) st.template load<true>(rows, c + 256, ahead);
+      if (c + 128 < tok1) st.template load<true>(rows, c + 128, ahead);
       st.template compute<true>(rows, c, cur, ks[c >> 5] * a.scale_log2, vs[c >> 5]);
     };
     int c0 = tok0 + 32 * w;
     if (c0 < tok1) {
-      Raw r0, r1, r2;
+      Raw r0, r1;
       st.template load<true>(rows, c0, r0);
-      if (c0 + 128 < tok1) st.template load<true>(rows, c0 + 128, r1);
-      for (;; c0 += 384) {
-        step(c0, r0, r2);
+      for (;; c0 += 256) {
+        step(c0, r0, r1);
         if (c0 + 128 >= tok1) break;
         step(c0 + 128, r1, r0);
         if (c0 + 256 >= tok1) break;
-        step(c0 + 256, r2, r1);
-        if (c0 + 384 >= tok1) break;
       }
     }
-  } else {
-    const int tok0 = (split - a.ns8) * a.splith;
-    const int tok1 = min(a.Th, tok0 + a.splith);
+  }
+  if (h0 < h1) {
+    const int tok0 = h0, tok1 = h1;
     const Bf16Rows<D> rows{a.kh + (size_t)unit * a.Th * D, a.vh + (size_t)unit * a.Th * D, tok1};
     for (int c0 = tok0 + 32 * w; c0 < tok1; c0 += 128) st.template chunk<false>(rows, c0, a.scale_log2, 1.f);
   }
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(D) void int8_combine_kernel(Int8DecodeArgs a) {
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int G = a.Hq / a.Hkv;
   const int unit = b * a.Hkv + h / G, head = h % G;
-  const int nsplit = a.ns8 + a.nsh;
+  const int nsplit = a.nsplit;
   const int t = threadIdx.x;
   const float* base = a.ws + (size_t)unit * nsplit * G * (D + 2) + (size_t)head * (D + 2);
   const size_t stride = (size_t)G * (D + 2);
@@ -239,22 +242,21 @@ __global__ __launch_bounds__(D) void int8_combine_kernel(Int8DecodeArgs a) {
 
 }  // namespace
 
-void int8_decode_plan(int B, int Hkv, int T8, int Th, int* split8, int* splith, int* ns8, int* nsh) {
+void int8_decode_plan(int B, int Hkv, int T8, int Th, int* nsplit, int* wsplit) {
+  // about DQ_TARGET_WGS workgroups in all, each range a multiple of 128 weights
+  // (128 INT8 tokens: one chunk per wave; 64 hot tokens)
   const long units = (long)B * Hkv;
-  const long T = (long)T8 + Th;
-  long want = (4096 + units - 1) / units;
+  const long wt = (long)T8 + 2l * Th;
+  long want = (DQ_TARGET_WGS + units - 1) / units;
   if (want < 1) want = 1;
-  long split = (T + want - 1) / want;
-  split = (split + 127) / 128 * 128;
-  if (split < 128) split = 128;
-  *split8 = (int)split;
-  *splith = (int)split;
-  *ns8 = T8 > 0 ? (int)((T8 + split - 1) / split) : 0;
-  *nsh = (int)((Th + split - 1) / split);
+  long ws = (wt + want - 1) / want;
+  ws = (ws + 127) / 128 * 128;
+  *wsplit = (int)ws;
+  *nsplit = (int)((wt + ws - 1) / ws);
 }
 
 hipError_t launch_int8_decode(const Int8DecodeArgs& a, hipStream_t s) {
-  const int grid = a.B * a.Hkv * (a.ns8 + a.nsh);
+  const int grid = a.B * a.Hkv * a.nsplit;
   if (a.D == 128) {
     hipLaunchKernelGGL(int8_decode_kernel<128>, dim3(grid), dim3(DQ_THREADS), 0, s, a);
     hipLaunchKernelGGL(int8_combine_kernel<128>, dim3(a.B * a.Hq), dim3(128), 0, s, a);
@@ -270,7 +272,7 @@ hipError_t launch_sparse_decode(const SparseDecodeArgs& a, hipStream_t s) {
   Int8DecodeArgs c{};  // the combine reads only these fields
   c.out = a.out; c.ws = a.ws;
   c.B = a.B; c.Hq = a.Hq; c.Hkv = a.Hkv; c.D = a.D;
-  c.ns8 = a.nss; c.nsh = a.nsh;
+  c.nsplit = a.nss + a.nsh;
   if (a.D == 128) {
     hipLaunchKernelGGL(int8_sparse_decode_kernel<128>, dim3(grid), dim3(DQ_THREADS), 0, s, a);
     hipLaunchKernelGGL(int8_combine_kernel<128>, dim3(a.B * a.Hq), dim3(128), 0, s, c);

@@ -68,8 +68,10 @@ struct Int8DecodeArgs {
   float* ws;           // partials [B*Hkv][nsplit][G][D + 2]
   int B, Hq, Hkv, D, T8, Th;
   float scale_log2;
-  int split8, splith;  // tokens per split in the int8 / hot region
-  int ns8, nsh;        // number of splits in each region
+  // Split plan: an INT8 token weighs 1 (its 256 bytes of K and V codes) and a
+  // hot token 2; split s covers weights [s wsplit, (s+1) wsplit) of the order
+  // INT8 tokens 0 .. T8-1, then hot tokens 0 .. Th-1.
+  int nsplit, wsplit;
 };
 
 struct BlockSparseArgs {
@@ -130,7 +132,7 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_ring(const RingCopyArgs& a, hipStream_t s);
 hipError_t launch_ring_decode(const RingDecodeArgs& a, hipStream_t s);
 hipError_t launch_quant_b32(const QuantArgs& a, hipStream_t s);
-void int8_decode_plan(int B, int Hkv, int T8, int Th, int* split8, int* splith, int* ns8, int* nsh);
+void int8_decode_plan(int B, int Hkv, int T8, int Th, int* nsplit, int* wsplit);
 hipError_t launch_int8_decode(const Int8DecodeArgs& a, hipStream_t s);
 hipError_t launch_blocksparse(const BlockSparseArgs& a, hipStream_t s);
 hipError_t launch_window_safe(const WindowSafeArgs& a, hipStream_t s);
