@@ -131,6 +131,26 @@ __global__ __launch_bounds__(256) void bs_scores_kernel(BlockSparseArgs a) {
 }
 
 // grid: Hq * nb / 4, four rows (waves) per workgroup; MAXG * 64 >= nb
+// one row's selection with MAXG key groups (64 candidates each per lane)
+template <int MAXG>
+__device__ __forceinline__ void bs_select_row(const double* row, int n, int topk, int32_t* out,
+                                              unsigned long long* gather) {
+  const int lane = __lane_id();
+  // every load unconditional from an in-range address, then the selects: a load
+  // under a per-lane condition is waited for where it is issued, one at a time
+  double v[MAXG];
+#pragma unroll
+  for (int i = 0; i < MAXG; ++i) v[i] = row[min(i * 64 + lane, n - 1)];
+  unsigned long long keys[MAXG];
+#pragma unroll
+  for (int i = 0; i < MAXG; ++i) keys[i] = i * 64 + lane < n ? order_key(v[i]) : 0ull;  // 0: below every key
+  const int written = topk_select_row<MAXG>(keys, n, topk, gather, [&](int slot, int kb) { out[slot] = kb; });
+  for (int i = written + lane; i < topk; i += 64) out[i] = -1;
+}
+
+// grid: ceil(Hq * nb / 4); wave w of block x selects row 4x + w, its key groups
+// sized to the row (8, 16, 32 or 64 groups of 64 candidates, at most MAXG: the
+// largest size sets the kernel's registers)
 template <int MAXG>
 __global__ __launch_bounds__(256) void bs_select_kernel(BlockSparseArgs a) {
   __shared__ unsigned long long gather[4][64];
@@ -147,15 +167,10 @@ __global__ __launch_bounds__(256) void bs_select_kernel(BlockSparseArgs a) {
     return;
   }
   const double* row = a.scores + tri_row(a, h, qb);
-  const int ngr = (n + 63) >> 6;
-  unsigned long long keys[MAXG];
-#pragma unroll
-  for (int i = 0; i < MAXG; ++i) {
-    const int kb = i * 64 + lane;
-    keys[i] = (i < ngr && kb < n) ? order_key(row[kb]) : 0ull;  // 0 sorts below every key
-  }
-  const int written = topk_select_row<MAXG>(keys, ngr, n, topk, gather[w], [&](int slot, int kb) { out[slot] = kb; });
-  for (int i = written + lane; i < topk; i += 64) out[i] = -1;
+  if (n <= 512) bs_select_row<8>(row, n, topk, out, gather[w]);
+  else if (n <= 1024) bs_select_row<16>(row, n, topk, out, gather[w]);
+  else if (MAXG <= 32 || n <= 2048) bs_select_row<MAXG <= 32 ? MAXG : 32>(row, n, topk, out, gather[w]);
+  else bs_select_row<64>(row, n, topk, out, gather[w]);
 }
 
 // Number of tile stages of the attend kernel; NST stages keep NST-1 tiles in

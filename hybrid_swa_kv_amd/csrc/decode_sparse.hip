@@ -39,29 +39,58 @@ __global__ __launch_bounds__(256) void int8_block_means_kernel(BlockMeansArgs a)
   a.means[((size_t)unit * a.D + d) * nblk + blk] = prod * (1.0f / BLK);  // exact
 }
 
-// grid: B * Hkv * ceil(nblk / 64); 4 waves: lane l of wave w scores block
-// 64 tile + l for heads w, w+4, ... of the group (fp64, one FMA chain over d)
+// grid: B * Hkv * ceil(nblk / 256); lane t of the workgroup scores block
+// 256 tile + t for every head of the group.  The block's means are read once,
+// 16 d at a time with the next 16 in flight, and NH chains of fp64 FMAs (one per
+// head, d ascending; heads past G have zero q rows) consume them.
+template <int D, int NH>
 __global__ __launch_bounds__(256) void int8_sparse_scores_kernel(SparseDecodeArgs a) {
-  __shared__ double qd[16 * 128];  // the group's q as fp64, [G][D]
+  constexpr int DC = 16;  // means per chunk
+  __shared__ float4 q4[NH * D / 4];  // the group's q as fp32 (exact for bf16), [head][d / 4]
   const int G = a.Hq / a.Hkv;
-  const int ntile = (a.nblk + 63) / 64;
+  const int ntile = (a.nblk + 255) / 256;
   const int unit = blockIdx.x / ntile, tile = blockIdx.x % ntile;
   const int b = unit / a.Hkv, g = unit % a.Hkv;
-  const int w = threadIdx.x >> 6, lane = __lane_id();
-  for (int i = threadIdx.x; i < G * a.D; i += blockDim.x) {
-    const int hh = i / a.D, d = i % a.D;
-    qd[i] = (double)bf16_to_f32(a.q[((size_t)b * a.Hq + g * G + hh) * a.D + d]);
+  float* qf = (float*)q4;
+  for (int i = threadIdx.x; i < NH * D; i += blockDim.x) {
+    const int hh = i / D, d = i % D;
+    qf[i] = hh < G ? bf16_to_f32(a.q[((size_t)b * a.Hq + g * G + hh) * D + d]) : 0.f;
   }
+  const int j = tile * 256 + threadIdx.x;
+  const float* mcol = a.means + (size_t)unit * D * a.nblk + min(j, a.nblk - 1);  // in range
+  const size_t st = a.nblk;
+  auto load = [&](int c, float (&m)[DC]) {
+#pragma unroll
+    for (int k = 0; k < DC; ++k) m[k] = mcol[(size_t)(c * DC + k) * st];
+  };
+  double sc[NH];
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) sc[hh] = 0.0;
+  auto use = [&](int c, const float (&m)[DC]) {
+#pragma unroll
+    for (int k4 = 0; k4 < DC / 4; ++k4)
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) {
+        const float4 qv = q4[hh * (D / 4) + c * (DC / 4) + k4];
+        sc[hh] = fma((double)qv.x, (double)m[4 * k4 + 0], sc[hh]);
+        sc[hh] = fma((double)qv.y, (double)m[4 * k4 + 1], sc[hh]);
+        sc[hh] = fma((double)qv.z, (double)m[4 * k4 + 2], sc[hh]);
+        sc[hh] = fma((double)qv.w, (double)m[4 * k4 + 3], sc[hh]);
+      }
+  };
+  float m0[DC], m1[DC];
+  load(0, m0);
   __syncthreads();
-  const int j = tile * 64 + lane;
-  if (j >= a.nblk) return;
-  const float* mcol = a.means + (size_t)unit * a.D * a.nblk + j;
-  for (int hh = w; hh < G; hh += 4) {
-    const double* qh = qd + hh * a.D;
-    double sc = 0.0;
-    for (int d = 0; d < a.D; ++d) sc = fma(qh[d], (double)mcol[(size_t)d * a.nblk], sc);
-    a.scores[((size_t)b * a.Hq + g * G + hh) * a.nblk + j] = sc;
+  for (int c = 0; c < D / DC; c += 2) {
+    load(c + 1, m1);  // D / DC is even
+    use(c, m0);
+    if (c + 2 < D / DC) load(c + 2, m0);
+    use(c + 1, m1);
   }
+  if (j >= a.nblk) return;
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh)
+    if (hh < G) a.scores[((size_t)b * a.Hq + g * G + hh) * a.nblk + j] = sc[hh];
 }
 
 // grid: B * Hkv; 4 waves, wave w serving heads w, w+4, ... of the group (G <= 16);
@@ -88,14 +117,15 @@ __global__ __launch_bounds__(256) void int8_sparse_select_kernel(SparseDecodeArg
       continue;
     }
     const double* sr = a.scores + row * nblk;
-    const int ngr = (nblk + 63) >> 6;
+    // every load unconditional from an in-range address, then the selects (a
+    // load under a per-lane condition is waited for where it is issued)
+    double v[MAXG];
+#pragma unroll
+    for (int i = 0; i < MAXG; ++i) v[i] = sr[min(i * 64 + lane, nblk - 1)];
     unsigned long long keys[MAXG];
 #pragma unroll
-    for (int i = 0; i < MAXG; ++i) {
-      const int j = i * 64 + lane;
-      keys[i] = (i < ngr && j < nblk) ? order_key(sr[j]) : 0ull;  // absent: below every key
-    }
-    const int written = topk_select_row<MAXG>(keys, ngr, nblk, topk, gather[w], [&](int slot, int j) {
+    for (int i = 0; i < MAXG; ++i) keys[i] = i * 64 + lane < nblk ? order_key(v[i]) : 0ull;  // absent: 0
+    const int written = topk_select_row<MAXG>(keys, nblk, topk, gather[w], [&](int slot, int j) {
       out[slot] = j;
       atomicOr(&hb[j], 1u << hh);
     });
@@ -132,14 +162,30 @@ hipError_t launch_block_means(const BlockMeansArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_sparse_select(const SparseDecodeArgs& a, hipStream_t s) {
-  const int ntile = (a.nblk + 63) / 64;
-  if (a.nblk > a.topk)
-    hipLaunchKernelGGL(int8_sparse_scores_kernel, dim3(a.B * a.Hkv * ntile), dim3(256), 0, s, a);
+  if (a.nblk > a.topk) {
+    const dim3 grid(a.B * a.Hkv * ((a.nblk + 255) / 256));
+    const int G = a.Hq / a.Hkv;  // <= 16, checked at the boundary
+    if (a.D == 128) {
+      if (G <= 4) hipLaunchKernelGGL((int8_sparse_scores_kernel<128, 4>), grid, dim3(256), 0, s, a);
+      else if (G <= 8) hipLaunchKernelGGL((int8_sparse_scores_kernel<128, 8>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((int8_sparse_scores_kernel<128, 16>), grid, dim3(256), 0, s, a);
+    } else {
+      if (G <= 4) hipLaunchKernelGGL((int8_sparse_scores_kernel<64, 4>), grid, dim3(256), 0, s, a);
+      else if (G <= 8) hipLaunchKernelGGL((int8_sparse_scores_kernel<64, 8>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((int8_sparse_scores_kernel<64, 16>), grid, dim3(256), 0, s, a);
+    }
+  }
+  // key groups of 64 candidates per lane: the smallest of 8, 16, 32, 64 that holds nblk (<= 4096)
   const size_t dyn = (size_t)a.nblk * sizeof(unsigned);
+  const dim3 grid(a.B * a.Hkv);
   if (a.nblk > 2048)
-    hipLaunchKernelGGL((int8_sparse_select_kernel<64>), dim3(a.B * a.Hkv), dim3(256), dyn, s, a);
+    hipLaunchKernelGGL((int8_sparse_select_kernel<64>), grid, dim3(256), dyn, s, a);
+  else if (a.nblk > 1024)
+    hipLaunchKernelGGL((int8_sparse_select_kernel<32>), grid, dim3(256), dyn, s, a);
+  else if (a.nblk > 512)
+    hipLaunchKernelGGL((int8_sparse_select_kernel<16>), grid, dim3(256), dyn, s, a);
   else
-    hipLaunchKernelGGL((int8_sparse_select_kernel<32>), dim3(a.B * a.Hkv), dim3(256), dyn, s, a);
+    hipLaunchKernelGGL((int8_sparse_select_kernel<8>), grid, dim3(256), dyn, s, a);
   return hipGetLastError();
 }
 

@@ -13,22 +13,24 @@ __device__ __forceinline__ unsigned long long order_key(double x) {
 }
 
 // Candidates 0 .. n-1 of one row, lane l holding candidate 64 i + l in keys[i]
-// (i < ngr; absent candidates hold key 0, below every real key).  Keeps the topk
-// largest keys, ties to the lower index: the threshold T is the largest key with
+// (n <= 64 MAXG; absent candidates hold key 0, below every real key, and every
+// threshold tried is above 0, so they never count).  Keeps the topk largest keys,
+// ties to the lower index: the threshold T is the largest key with
 // #{key >= T} >= topk, searched over the top 16 bits first and then over the
 // candidates sharing that 16-bit prefix (gathered one per lane through `gather`,
 // 64 words of LDS owned by this wave; the full search remains for rows with more
 // than 64 of them).  Calls emit(slot, index) for every kept candidate, slot being
 // its rank in ascending index order; returns how many were kept.  Needs n > topk.
+// Every loop runs over all MAXG groups with no per-group condition: a runtime
+// group count made each group a branch of its own.
 template <int MAXG, class Emit>
-__device__ __forceinline__ int topk_select_row(const unsigned long long (&keys)[MAXG], int ngr, int n, int topk,
+__device__ __forceinline__ int topk_select_row(const unsigned long long (&keys)[MAXG], int n, int topk,
                                                unsigned long long* gather, Emit emit) {
   const int lane = __lane_id();
   auto count_ge = [&](unsigned long long c) {
     int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < MAXG; ++i)
-      if (i < ngr) cnt += __popcll(__ballot(keys[i] >= c));
+    for (int i = 0; i < MAXG; ++i) cnt += __popcll(__ballot(keys[i] >= c));
     return cnt;
   };
   // 1. the top 16 bits over every candidate
@@ -44,7 +46,6 @@ __device__ __forceinline__ int topk_select_row(const unsigned long long (&keys)[
   int neq = 0;
 #pragma unroll
   for (int i = 0; i < MAXG; ++i) {
-    if (i >= ngr) continue;
     const bool eq = (keys[i] >> 48) == pre && keys[i] != 0ull;
     const unsigned long long m = __ballot(eq);
     const int pos = neq + __popcll(m & lt_mask);
@@ -66,13 +67,11 @@ __device__ __forceinline__ int topk_select_row(const unsigned long long (&keys)[
   }
   int gt = 0;
 #pragma unroll
-  for (int i = 0; i < MAXG; ++i)
-    if (i < ngr) gt += __popcll(__ballot(keys[i] > T));
+  for (int i = 0; i < MAXG; ++i) gt += __popcll(__ballot(keys[i] > T));
   const int need = topk - gt;
   int eq_before = 0, written = 0;
 #pragma unroll
   for (int i = 0; i < MAXG; ++i) {
-    if (i >= ngr) continue;
     const int kb = i * 64 + lane;
     const bool valid = kb < n;
     const bool is_gt = valid && keys[i] > T;
