@@ -31,7 +31,7 @@ constexpr int DQ_TARGET_WGS = 2048;  // workgroups of the dense INT8 decode in a
 template <int D>
 __global__ __launch_bounds__(DQ_THREADS, 3) void int8_decode_kernel(Int8DecodeArgs a) {
   __shared__ float sm_m[4][16], sm_l[4][16];
-  __shared__ float sm_o[4][16][D + 1];
+  __shared__ __attribute__((aligned(16))) float sm_o[4][16][stash_row<D>()];
 
   const int nsplit = a.nsplit;
   const int unit = blockIdx.x / nsplit;  // b * Hkv + g
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(DQ_THREADS, 3) void int8_decode_kernel(Int8DecodeAr
 template <int D>
 __global__ __launch_bounds__(DQ_THREADS) void int8_sparse_decode_kernel(SparseDecodeArgs a) {
   __shared__ float sm_m[4][16], sm_l[4][16];
-  __shared__ float sm_o[4][16][D + 1];
+  __shared__ __attribute__((aligned(16))) float sm_o[4][16][stash_row<D>()];
 
   const int nsplit = a.nss + a.nsh;
   const int nhot = a.B * a.Hkv * a.nsh;

@@ -57,6 +57,12 @@ __device__ __forceinline__ uint2 sel2(uint2 a, uint2 b, unsigned m) {
 //   true:  d = 64 kk + 32 e + 8 g + j (bf16 rows: each load instruction then reads
 //          64 contiguous bytes of a row instead of 16 bytes every 32)
 // Any consistent assignment of d to the contraction slots gives the same scores.
+// Row length of a stashed wave state in LDS: D floats padded to a multiple of
+// 16 bytes plus 16, so each head's row starts 16-byte aligned (128-bit stores)
+// and the rows of neighbouring heads start in different banks.
+template <int D>
+constexpr int stash_row() { return D + 4; }
+
 template <int D, bool BLOCKED = false>
 struct DecodeWave {
   static constexpr int NK = D / 64;
@@ -191,8 +197,10 @@ struct DecodeWave {
 
   // alt: the replacing row (used when Rows::kHasAlt and it falls in this chunk)
   template <bool INT8, int NT = 2, class Rows>
+  // first: this is the wave's first chunk (o and l are still zero, m is -inf), so
+  // the offset is simply the chunk's maximum and nothing needs rescaling
   __device__ __forceinline__ void compute(const Rows& rows, int c0, Raw<INT8>& raw, float sk, float sv,
-                                          const AltRow& alt, unsigned head_bits = ~0u) {
+                                          const AltRow& alt, unsigned head_bits = ~0u, bool first = false) {
     const int lane = __lane_id();
     const int hl = lane & 15, gq = lane >> 4;
     constexpr int KV = Raw<INT8>::KV;
@@ -310,7 +318,9 @@ struct DecodeWave {
     // Lazy offset: m only moves when a head's maximum grows by more than 8 (a
     // factor 256 in the log2 domain), so most chunks skip the accumulator rescale;
     // numerator and denominator always share m.
-    if (__any(mx > m + 8.f)) {
+    if (first) {
+      m = mx;
+    } else if (__any(mx > m + 8.f)) {
       const float m_new = fmaxf(m, mx);
       const float alpha = (m == kNegInf) ? 0.f : fast_exp2(m - m_new);
       l *= alpha;
@@ -351,9 +361,9 @@ struct DecodeWave {
   }
 
   // Write this wave's state for the heads it serves (lane%16 < G) to LDS:
-  // sm_m/sm_l [waves][16], sm_o [waves][16][D + 1] (rows padded by one float so
-  // the 16 heads written by one instruction fall in different banks).
-  __device__ __forceinline__ void stash(float (*sm_m)[16], float (*sm_l)[16], float (*sm_o)[16][D + 1],
+  // sm_m/sm_l [waves][16], sm_o [waves][16][stash_row<D>()]; a lane's four
+  // jj values of one (hv, r) are adjacent columns, stored as one 128-bit write.
+  __device__ __forceinline__ void stash(float (*sm_m)[16], float (*sm_l)[16], float (*sm_o)[16][stash_row<D>()],
                                         int w, int G) {
     const int lane = __lane_id();
     const int hl = lane & 15, gq = lane >> 4;
@@ -364,9 +374,9 @@ struct DecodeWave {
 #pragma unroll
       for (int hv = 0; hv < NK; ++hv)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sm_o[w][hl][64 * hv + 16 * gq + 4 * r + jj] = o[hv][jj][r];
+        for (int r = 0; r < 4; ++r)
+          *(float4*)&sm_o[w][hl][64 * hv + 16 * gq + 4 * r] =
+              make_float4(o[hv][0][r], o[hv][1][r], o[hv][2][r], o[hv][3][r]);
       if (gq == 0) {
         sm_m[w][hl] = m;
         sm_l[w][hl] = lsum;
@@ -378,7 +388,7 @@ struct DecodeWave {
 // Merge NW stashed wave states for (head, d): returns acc, sets M and Lsum.
 template <int NW, int D>
 __device__ __forceinline__ float merge_waves(const float (*sm_m)[16], const float (*sm_l)[16],
-                                             const float (*sm_o)[16][D + 1], int head, int d,
+                                             const float (*sm_o)[16][stash_row<D>()], int head, int d,
                                              float& M, float& Ls) {
   M = kNegInf;
 #pragma unroll

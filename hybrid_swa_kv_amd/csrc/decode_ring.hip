@@ -28,7 +28,7 @@ constexpr int RD_STRIDE = RD_CHUNK * RD_WAVES;   // slots per workgroup step
 template <int D>
 __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs a) {
   __shared__ float sm_m[RD_WAVES][16], sm_l[RD_WAVES][16];
-  __shared__ float sm_o[RD_WAVES][16][D + 1];
+  __shared__ __attribute__((aligned(16))) float sm_o[RD_WAVES][16][stash_row<D>()];
   __shared__ __attribute__((aligned(16))) uint16_t sm_in[(16 + 2) * D];
 
   const int G = a.Hq / a.Hkv;
@@ -90,11 +90,11 @@ __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs 
   int c0 = first;
   for (; c0 + RD_STRIDE < W; c0 += 2 * RD_STRIDE) {
     st.template load<false, 1>(rows, c0 + RD_STRIDE, nxt);
-    st.template compute<false, 1>(rows, c0, cur, a.scale_log2, 1.f, alt);
+    st.template compute<false, 1>(rows, c0, cur, a.scale_log2, 1.f, alt, ~0u, c0 == first);
     if (c0 + 2 * RD_STRIDE < W) st.template load<false, 1>(rows, c0 + 2 * RD_STRIDE, cur);
     st.template compute<false, 1>(rows, c0 + RD_STRIDE, nxt, a.scale_log2, 1.f, alt);
   }
-  if (c0 < W) st.template compute<false, 1>(rows, c0, cur, a.scale_log2, 1.f, alt);
+  if (c0 < W) st.template compute<false, 1>(rows, c0, cur, a.scale_log2, 1.f, alt, ~0u, c0 == first);
 
   st.stash(sm_m, sm_l, sm_o, w, HG);
   __syncthreads();
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs 
     const int head = e / D, d = e % D;
     float M, Ls;
     const float O = merge_waves<RD_WAVES, D>(sm_m, sm_l, sm_o, head, d, M, Ls);
-    a.out[((size_t)b * a.Hq + h0 + head) * D + d] = f32_to_bf16(ok ? O / Ls : 0.f);
+    a.out[((size_t)b * a.Hq + h0 + head) * D + d] = f32_to_bf16(ok ? O * __builtin_amdgcn_rcpf(Ls) : 0.f);
   }
 }
 
