@@ -203,6 +203,7 @@ int kv_quant_int8_b32(const void* x, int8_t* codes, float* scales, int B, int Hk
 
 size_t attn_decode_int8kv_workspace_size(int B, int Hq, int Hkv, int D, int T8, int Th) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || T8 < 0 || Th <= 0) return 0;
+  if ((long long)T8 + 2ll * Th >= (1ll << 31)) return 0;
   return int8_ws_bytes(B, Hq, Hkv, D, T8, Th);
 }
 
@@ -216,6 +217,7 @@ int attn_decode_int8kv(const void* q, const int8_t* k_codes, const float* k_scal
   if (int rc = check_heads(Hq, Hkv, D)) return rc;
   if (Hq / Hkv > 16) return HSK_ERR_UNSUPPORTED;
   if ((long long)T8 * D >= (1ll << 31)) return HSK_ERR_UNSUPPORTED;  // 32-bit code offsets per head
+  if ((long long)T8 + 2ll * Th >= (1ll << 31)) return HSK_ERR_UNSUPPORTED;  // 32-bit split weights
   if (!std::isfinite(scale)) return HSK_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_hot) || !aligned16(v_hot) || !aligned16(out)) return HSK_ERR_ALIGN;
   if (T8 > 0 && (!aligned16(k_codes) || !aligned16(v_codes) || !aligned4(k_scales) || !aligned4(v_scales)))

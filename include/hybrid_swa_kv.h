@@ -161,8 +161,8 @@ int kv_quant_int8_b32(const void* x, int8_t* codes, float* scales,
  * k_hot, v_hot     [B, Hkv, Th, D] bf16     (Th >= 1)
  * out              [B, Hq, D] bf16, written
  * workspace        device scratch of attn_decode_int8kv_workspace_size(...) bytes
- * Limits: Hq / Hkv <= 16 and T8 * D < 2^31 per (sequence, KV head), else
- * HSK_ERR_UNSUPPORTED.
+ * Limits: Hq / Hkv <= 16, T8 * D < 2^31 and T8 + 2 Th < 2^31 per (sequence,
+ * KV head), else HSK_ERR_UNSUPPORTED (the workspace size query returns 0).
  */
 int attn_decode_int8kv(const void* q,
                        const int8_t* k_codes, const float* k_scales,

@@ -87,11 +87,13 @@ def test_int8_decode_validation(lib):
     need = lib.attn_decode_int8kv_workspace_size(16, 32, 8, 128, 63488, 2048)
     assert need > 0
     assert lib.attn_decode_int8kv_workspace_size(16, 32, 8, 128, 63488, 0) == 0
+    assert lib.attn_decode_int8kv_workspace_size(1, 4, 1, 128, 0, 1 << 30) == 0  # weights past 2^31
     #        q kc ks vc vs kh vh out B Hq Hkv D T8 Th scale ws wsb stream
     assert f(P, None, P, P, P, P, P, P, 16, 32, 8, 128, 64, 8, 1.0, P, need, None) == NULL
     assert f(P, P, P, P, P, P, P, P, 16, 32, 8, 128, 48, 8, 1.0, P, need, None) == SHAPE
     assert f(P, P, P, P, P, P, P, P, 16, 32, 8, 128, 64, 0, 1.0, P, need, None) == SHAPE
     assert f(P, P, P, P, P, P, P, P, 1, 34, 2, 128, 64, 8, 1.0, P, need, None) == UNSUP
+    assert f(P, P, P, P, P, P, P, P, 1, 4, 1, 128, 0, 1 << 30, 1.0, P, need, None) == UNSUP
     assert f(P, P, P, P, P, P, P, P, 16, 32, 8, 128, 63488, 2048, 1.0, P, need - 1, None) == WS
     assert f(P, P, P, P, P, P, P, P, 16, 32, 8, 128, 63488, 2048, 1.0, None, need, None) == WS
     assert f(P, P, P, P, P, MIS, P, P, 16, 32, 8, 128, 63488, 2048, 1.0, P, need, None) == ALIGN
