@@ -177,12 +177,72 @@ def sparse_tile_bytes(sel, L: int, block: int, W: int, Hkv: int, D: int) -> int:
     return tiles * 2 * block * D * 2
 
 
+class ClockSampler:
+    """Engine clock (MHz) from the driver's pp_dpm_sclk (the line marked '*'),
+    sampled by a host thread; each sample carries its host time."""
+
+    def __init__(self):
+        import glob
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.samples = []
+        self._stop = None
+        self._th = None
+
+    def read(self):
+        import re
+        vals = []
+        for p in self.paths:
+            try:
+                for ln in open(p).read().splitlines():
+                    if ln.rstrip().endswith("*"):
+                        m = re.search(r"(\d+)\s*Mhz", ln, re.I)
+                        if m:
+                            vals.append(int(m.group(1)))
+            except OSError:
+                pass
+        return max(vals) if vals else None
+
+    def start(self):
+        import threading
+        if not self.paths:
+            return
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                v = self.read()
+                if v is not None:
+                    self.samples.append((time.perf_counter(), v))
+                time.sleep(0.0005)
+
+        self._th = threading.Thread(target=loop, daemon=True)
+        self._th.start()
+
+    def stop(self):
+        if self._th is not None:
+            self._stop.set()
+            self._th.join()
+
+    def per_window(self, windows):
+        """windows: (name, t_begin, t_end) in host time -> {name: clock stats}."""
+        out = {}
+        for name, a, b in windows:
+            out.setdefault(name, []).extend(v for t, v in self.samples if a <= t < b)
+        stats = {}
+        for name, v in out.items():
+            if v:
+                v = sorted(v)
+                stats[name] = {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v)}
+        return stats
+
+
 class Timer:
     """HIP events around work enqueued on torch's current stream (the library's stream)."""
 
     def __init__(self, torch):
         self.torch = torch
         self.ms = {}
+        self.order = []  # (name, end event) in enqueue order
 
     def run(self, name, fn):
         t = self.torch
@@ -191,6 +251,7 @@ class Timer:
         fn()
         b.record()
         self.ms.setdefault(name, []).append((a, b))
+        self.order.append((name, b))
 
     def mean_ms(self, name, skip=0):
         ev = self.ms[name][skip:]
@@ -434,12 +495,25 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     print("[bench] timing", file=sys.stderr, flush=True)
+    clock = ClockSampler()
+    timer.order.clear()
+    clock.start()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step()
         print(f"[bench] step {i + 1}/{args.steps} enqueued", file=sys.stderr, flush=True)
+    # wait for each row's end in GPU order, noting when it completes: the engine
+    # clock samples between two completions belong to the row that ended second
+    windows, prev = [], t0
+    for name, ev in timer.order:
+        ev.synchronize()
+        now = time.perf_counter()
+        windows.append((name, prev, now))
+        prev = now
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock.stop()
+    sclk = clock.per_window(windows)
     ms_step = wall * 1e3 / args.steps
 
     res = {}
@@ -525,6 +599,11 @@ def main() -> int:
                            "full_layer_us": round(full_us, 2),
                            "kv_bytes_ratio_vs_all_full": round(step_bytes / all_full_bytes, 4),
                            "time_ratio_vs_all_full": round(ms * 1e3 / (c["layers"] * full_us), 4)}
+
+    # the engine clock sampled while each row ran in the timed steps
+    for name, st in sclk.items():
+        if name in res and isinstance(res[name], dict):
+            res[name]["sclk_mhz"] = st
 
     line = {
         "metric": METRIC,
