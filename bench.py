@@ -310,8 +310,8 @@ def main() -> int:
                          "scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); the path has no "
-              "multi-GPU component in this build", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}): the kernels work on "
+              "one GPU's share; how they would shard is described, not implemented", file=sys.stderr)
         return 2
     rows = [r for r in args.rows.split(",") if r]
 
