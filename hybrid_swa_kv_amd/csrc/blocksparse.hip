@@ -173,15 +173,15 @@ __global__ __launch_bounds__(256) void bs_select_kernel(BlockSparseArgs a) {
   else bs_select_row<64>(row, n, topk, out, gather[w]);
 }
 
-// Number of tile stages of the attend kernel; NST stages keep NST-1 tiles in
-// flight per workgroup.  Two stages (64 KB of LDS at D = 128) leave room for two
+// The attend kernel double-buffers its tiles: one tile in flight while the other
+// is computed.  Two stages (64 KB of LDS at D = 128) leave room for two
 // workgroups per CU; three or four stages keep more tiles in flight but fit one
-// workgroup per CU and measure about 1.7x slower.
-constexpr int NST = 2;
-
-// Stage s of the ring, one __shared__ object each: slices of a single array
-// would make the compiler wait for every outstanding tile DMA before each LDS
-// read, since it could not tell the stages apart.
+// workgroup per CU and measured about 1.7x slower; a single stage with four
+// workgroups per CU measured 7 % slower.
+//
+// Stage S, one __shared__ object each: slices of a single array would make the
+// compiler wait for every outstanding tile DMA before each LDS read, since it
+// could not tell the stages apart.
 template <int D, int S>
 __device__ __forceinline__ char* bs_stage() {
   __shared__ __attribute__((aligned(16))) char buf[2 * FtCfg<D>::TILE];
@@ -192,7 +192,6 @@ __device__ __forceinline__ char* bs_stage() {
 template <int D>
 __global__ __launch_bounds__(AT_THREADS) void bs_attend_kernel(BlockSparseArgs a) {
   using C = FtCfg<D>;
-  static_assert(NST >= 2 && NST <= 4, "2 to 4 stages");
   __shared__ int list[256];                  // selected blocks before the window
   __shared__ unsigned selbits[SEL_MAXNB / 32];
   __shared__ int s_npre;
@@ -245,31 +244,25 @@ __global__ __launch_bounds__(AT_THREADS) void bs_attend_kernel(BlockSparseArgs a
   // the tile index is uniform; saying so keeps the DMA offset scalar (an LDS value
   // would otherwise count as per-lane and the DMA would loop over lanes)
   auto tile_of = [&](int it) { return __builtin_amdgcn_readfirstlane(it < npre ? list[it] : kw0 + (it - npre)); };
-  char* const stage[4] = {bs_stage<D, 0>(), bs_stage<D, 1>(), bs_stage<D, 2>(), bs_stage<D, 3>()};
-#pragma unroll
-  for (int p = 0; p < NST - 1; ++p)
-    if (p < ntiles) dma.issue(tile_of(p), stage[p]);
-  constexpr int PER_TILE = 2 * TileDma<D, AT_THREADS>::PER_WAVE;  // DMA instructions per tile per wave
-  // unrolled by NST so that every stage address is a compile-time constant
-  for (int it0 = 0; it0 < ntiles; it0 += NST) {
-#pragma unroll
-    for (int j = 0; j < NST; ++j) {
-      const int it = it0 + j;
-      if (it < ntiles) {
-        // tile it has landed once at most the later tiles' DMAs are outstanding
-        const int later = min(ntiles - 1 - it, NST - 2);
-        if (NST >= 4 && later >= 2) wait_vmem_upto<2 * PER_TILE>();
-        else if (NST >= 3 && later >= 1) wait_vmem_upto<PER_TILE>();
-        else wait_vmem_upto<0>();
-        lds_barrier();  // ... for every wave; and tile it-1's stage is free
-        const int kt = tile_of(it);
-        if (it + NST - 1 < ntiles) dma.issue(tile_of(it + NST - 1), stage[(j + NST - 1) % NST]);
-        const char* ks = stage[j];
-        const bool full = (selbits[kt >> 5] >> (kt & 31)) & 1u;
-        fw.tile(ks, ks + C::TILE, kt * FT_BN, r0, row, W, full, a.scale_log2);
-      }
-    }
+  char* const s0 = bs_stage<D, 0>();
+  char* const s1 = bs_stage<D, 1>();
+  dma.issue(tile_of(0), s0);  // ntiles >= 1: the window holds the query block itself
+  // one tile step: tile it is in cur, tile it+1 goes to nxt
+  auto step = [&](int it, char* cur, char* nxt) {
+    wait_vmem();    // this wave's part of tile it has landed
+    lds_barrier();  // ... everyone's has, and tile it-1's stage is free
+    const int kt = tile_of(it);
+    if (it + 1 < ntiles) dma.issue(tile_of(it + 1), nxt);
+    const bool full = (selbits[kt >> 5] >> (kt & 31)) & 1u;
+    fw.tile(cur, cur + C::TILE, kt * FT_BN, r0, row, W, full, a.scale_log2);
+  };
+  // unrolled by two so that every stage address is a compile-time constant
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    step(it, s0, s1);
+    step(it + 1, s1, s0);
   }
+  if (it < ntiles) step(it, s0, s1);
   fw.store(a.out + ((size_t)row * a.Hq + h) * D);
 }
 

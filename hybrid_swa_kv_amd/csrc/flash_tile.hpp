@@ -99,15 +99,6 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// Wait until at most N of this wave's vector-memory operations are outstanding
-// (they complete in issue order): s_waitcnt with vmcnt = N (bits 3:0 and 15:14),
-// expcnt and lgkmcnt left at their maximum.
-template <int N>
-__device__ __forceinline__ void wait_vmem_upto() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
 // Workgroup barrier for the tile loops.  This wave's LDS reads complete first
 // (lgkmcnt 0); there is no memory fence, so the tile DMAs still in flight stay
 // in flight (the caller has already waited for the ones it needs).  The memory
