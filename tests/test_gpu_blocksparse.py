@@ -52,6 +52,25 @@ def test_blocksparse_parity(L, Hq, Hkv, D, topk, window):
     assert ex <= 0, (ex, max_abs(out_f64(out), ref))
 
 
+def test_blocksparse_past_2048_blocks():
+    """2176 key blocks: rows with more than 2048 candidates take the widest
+    selection path; every selection checked, attention on sampled rows."""
+    L, Hq, Hkv, D, topk, window = 64 * 2176, 2, 1, 64, 8, 64
+    announce("blocksparse_2176_blocks", L=L)
+    q = synth.token_major(97, synth.Q, L, Hq, D)
+    k = synth.token_major(97, synth.K, L, Hkv, D)
+    v = synth.token_major(97, synth.V, L, Hkv, D)
+    out, sel = hsk.blocksparse_select_attend(gpu_bf16(q), gpu_bf16(k), gpu_bf16(v), 64, topk, window)
+    sel_np = sel.cpu().numpy()
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    check_selection(sel_np, qf, kf, 64, topk)
+    rows = np.array([0, 63, 64, 131071, 131072, 131135, 131136, 139263, 100000, 135000], dtype=np.int64)
+    got = out_f64(out)[rows]
+    ref = oracle.blocksparse_attend(qf, kf, vf, sel_np, 64, window, rows=rows)
+    ex = bf16_excess(got, ref)
+    assert ex <= 0, (ex, max_abs(got, ref))
+
+
 def test_blocksparse_exact_tie():
     # duplicate key blocks produce exactly equal scores: the lower block must win
     L, Hq, Hkv, D, topk = 1024, 2, 1, 128, 2

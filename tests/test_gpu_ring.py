@@ -65,7 +65,7 @@ def test_ring_positions(W):
     run_case(20 + W, B, 8, 2, 128, W, pos)
 
 
-@pytest.mark.parametrize("Hq,Hkv,D", [(4, 4, 64), (16, 1, 128), (12, 4, 128), (32, 2, 64)])
+@pytest.mark.parametrize("Hq,Hkv,D", [(4, 4, 64), (16, 1, 128), (12, 4, 128), (32, 2, 64), (64, 2, 128)])
 def test_ring_heads(Hq, Hkv, D):
     announce("ring_heads", Hq=Hq, Hkv=Hkv, D=D)
     rng = np.random.default_rng(Hq * 10 + D)

@@ -59,6 +59,7 @@ def check_rows(sel_gpu, scores, topk, rows):
     (2, 8, 2, 128, 640, 64, 0),        # no block kept: the hot tail alone
     (2, 8, 2, 128, 0, 70, 16),         # no INT8 region
     (1, 8, 2, 128, 131072, 32, 64),    # 4096 blocks
+    (1, 8, 1, 128, 22400, 64, 16),     # 700 blocks, 8 heads per group
 ])
 def test_sparse_decode_parity(B, Hq, Hkv, D, T8, Th, topk):
     announce("sparse_decode", B=B, Hq=Hq, Hkv=Hkv, D=D, T8=T8, Th=Th, topk=topk)
