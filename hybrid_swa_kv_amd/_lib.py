@@ -6,6 +6,7 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhybrid_swa_kv.so")
+ABI_VERSION = 4  # the signatures below; hsk_abi_version() of the loaded library must match
 
 # every symbol declared in include/hybrid_swa_kv.h
 EXPORTS = (
@@ -61,5 +62,9 @@ def load() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
+        got = lib.hsk_abi_version()
+        if got != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {got}, these bindings expect {ABI_VERSION}: "
+                               "rebuild it with `python -m hybrid_swa_kv_amd.build`")
         _lib = lib
     return _lib
