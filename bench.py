@@ -302,7 +302,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--rows", default="ring,swa,full,chunk4096,chunk8192,quant,int8,int8sparse,sparse,hybrid70")
+    ap.add_argument("--rows", default="ring,int8,int8sparse,quant,swa,full,chunk4096,chunk8192,sparse,hybrid70")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
