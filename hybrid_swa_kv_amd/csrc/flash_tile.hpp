@@ -44,53 +44,6 @@ __device__ __forceinline__ int ft_off(int row, int chunk) {
   return row * NCH * 16 + ((chunk ^ ft_swz<NCH>(row)) << 4);
 }
 
-// Global -> registers -> LDS staging of one K and one V tile by NT threads.
-template <int D, int NT>
-struct TileStage {
-  using C = FtCfg<D>;
-  static constexpr int CPT = FT_BN * C::NCH / NT;
-  uint4 kreg[CPT], vreg[CPT];
-
-  // rows kt*64 .. kt*64+63 of kbase/vbase (row stride in elements); rows >= nrows read as 0
-  __device__ __forceinline__ void load(const uint16_t* kbase, const uint16_t* vbase, size_t stride,
-                                       int kt, int nrows) {
-    const size_t tile_off = (size_t)kt * FT_BN * stride;
-    if ((kt + 1) * FT_BN <= nrows) {  // whole tile in range (uniform)
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const int u = i * NT + (int)threadIdx.x;
-        const size_t off = tile_off + (size_t)(u / C::NCH) * stride + (u % C::NCH) * 8;
-        kreg[i] = *(const uint4*)(kbase + off);
-        vreg[i] = *(const uint4*)(vbase + off);
-      }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int u = i * NT + (int)threadIdx.x;
-      const int r = u / C::NCH, c = u % C::NCH;
-      if (kt * FT_BN + r < nrows) {
-        const size_t off = tile_off + (size_t)r * stride + c * 8;
-        kreg[i] = *(const uint4*)(kbase + off);
-        vreg[i] = *(const uint4*)(vbase + off);
-      } else {
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(char* kv_lds) const {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int u = i * NT + (int)threadIdx.x;
-      const int r = u / C::NCH, c = u % C::NCH;
-      const int off = ft_off<C::NCH>(r, c);
-      *(uint4*)(kv_lds + off) = kreg[i];
-      *(uint4*)(kv_lds + C::TILE + off) = vreg[i];
-    }
-  }
-};
-
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Wait until this wave's vector-memory operations (here: LDS DMA loads) are done.
