@@ -36,6 +36,7 @@ constexpr int BS_BLOCK = 64;
 constexpr int SUM_THREADS = 256;
 constexpr int SEL_MAXNB = 4096;     // key blocks supported (L <= 262144 at block 64)
 constexpr int AT_THREADS = 128;
+constexpr int BS_FILTER = 8;      // pre-filtered candidate groups of the block selection
 
 // grid: nb (Q sums) + nb (K sums)
 __global__ __launch_bounds__(SUM_THREADS) void bs_sums_kernel(BlockSparseArgs a) {
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(256) void bs_scores_kernel(BlockSparseArgs a) {
 // one row's selection with MAXG key groups (64 candidates each per lane)
 template <int MAXG>
 __device__ __forceinline__ void bs_select_row(const double* row, int n, int topk, int32_t* out,
-                                              unsigned long long* gather) {
+                                              unsigned long long* gather, unsigned long long* fck, int* fci) {
   const int lane = __lane_id();
   // every load unconditional from an in-range address, then the selects: a load
   // under a per-lane condition is waited for where it is issued, one at a time
@@ -144,7 +145,9 @@ __device__ __forceinline__ void bs_select_row(const double* row, int n, int topk
   unsigned long long keys[MAXG];
 #pragma unroll
   for (int i = 0; i < MAXG; ++i) keys[i] = i * 64 + lane < n ? order_key(v[i]) : 0ull;  // 0: below every key
-  const int written = topk_select_row<MAXG>(keys, n, topk, gather, [&](int slot, int kb) { out[slot] = kb; });
+  const int written =
+      topk_select_row_filtered<BS_FILTER, MAXG>(keys, n, topk, gather, fck, fci,
+                                                [&](int slot, int kb) { out[slot] = kb; });
   for (int i = written + lane; i < topk; i += 64) out[i] = -1;
 }
 
@@ -154,6 +157,8 @@ __device__ __forceinline__ void bs_select_row(const double* row, int n, int topk
 template <int MAXG>
 __global__ __launch_bounds__(256) void bs_select_kernel(BlockSparseArgs a) {
   __shared__ unsigned long long gather[4][64];
+  __shared__ unsigned long long fck[4][64 * BS_FILTER];  // pre-filtered candidates
+  __shared__ int fci[4][64 * BS_FILTER];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = __lane_id();
   const int rowid = blockIdx.x * 4 + w;  // h * nb + qb
@@ -167,10 +172,11 @@ __global__ __launch_bounds__(256) void bs_select_kernel(BlockSparseArgs a) {
     return;
   }
   const double* row = a.scores + tri_row(a, h, qb);
-  if (n <= 512) bs_select_row<8>(row, n, topk, out, gather[w]);
-  else if (n <= 1024) bs_select_row<16>(row, n, topk, out, gather[w]);
-  else if (MAXG <= 32 || n <= 2048) bs_select_row<MAXG <= 32 ? MAXG : 32>(row, n, topk, out, gather[w]);
-  else bs_select_row<64>(row, n, topk, out, gather[w]);
+  if (n <= 512) bs_select_row<8>(row, n, topk, out, gather[w], fck[w], fci[w]);
+  else if (n <= 1024) bs_select_row<16>(row, n, topk, out, gather[w], fck[w], fci[w]);
+  else if (MAXG <= 32 || n <= 2048)
+    bs_select_row<MAXG <= 32 ? MAXG : 32>(row, n, topk, out, gather[w], fck[w], fci[w]);
+  else bs_select_row<64>(row, n, topk, out, gather[w], fck[w], fci[w]);
 }
 
 // The attend kernel double-buffers its tiles: one tile in flight while the other

@@ -99,6 +99,9 @@ template <int MAXG>
 __global__ __launch_bounds__(256) void int8_sparse_select_kernel(SparseDecodeArgs a) {
   extern __shared__ unsigned hb[];  // [nblk] head bits
   __shared__ unsigned long long gather[4][64];
+  constexpr int CF = 16;  // pre-filtered candidate groups (the slowest row sets this kernel's time)
+  __shared__ unsigned long long fck[4][64 * CF];
+  __shared__ int fci[4][64 * CF];
   const int G = a.Hq / a.Hkv;
   const int unit = blockIdx.x;
   const int b = unit / a.Hkv, g = unit % a.Hkv;
@@ -125,7 +128,8 @@ __global__ __launch_bounds__(256) void int8_sparse_select_kernel(SparseDecodeArg
     unsigned long long keys[MAXG];
 #pragma unroll
     for (int i = 0; i < MAXG; ++i) keys[i] = i * 64 + lane < nblk ? order_key(v[i]) : 0ull;  // absent: 0
-    const int written = topk_select_row<MAXG>(keys, nblk, topk, gather[w], [&](int slot, int j) {
+    const int written = topk_select_row_filtered<CF, MAXG>(keys, nblk, topk, gather[w], fck[w], fci[w],
+                                                       [&](int slot, int j) {
       out[slot] = j;
       atomicOr(&hb[j], 1u << hh);
     });

@@ -2,6 +2,8 @@
 // keys in registers, bit-by-bit threshold search with ballots).
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace hsk {
@@ -23,9 +25,13 @@ __device__ __forceinline__ unsigned long long order_key(double x) {
 // its rank in ascending index order; returns how many were kept.  Needs n > topk.
 // Every loop runs over all MAXG groups with no per-group condition: a runtime
 // group count made each group a branch of its own.
-template <int MAXG, class Emit>
-__device__ __forceinline__ int topk_select_row(const unsigned long long (&keys)[MAXG], int n, int topk,
-                                               unsigned long long* gather, Emit emit) {
+//
+// topk_core is the search with the candidate's index given by index_of(i) for the
+// lane's candidate of group i (positions i*64 + lane must be in ascending index
+// order); topk_select_row uses the position itself.
+template <int MAXG, class IndexOf, class Emit>
+__device__ __forceinline__ int topk_core(const unsigned long long (&keys)[MAXG], int n, int topk,
+                                         unsigned long long* gather, IndexOf index_of, Emit emit) {
   const int lane = __lane_id();
   auto count_ge = [&](unsigned long long c) {
     int cnt = 0;
@@ -72,8 +78,7 @@ __device__ __forceinline__ int topk_select_row(const unsigned long long (&keys)[
   int eq_before = 0, written = 0;
 #pragma unroll
   for (int i = 0; i < MAXG; ++i) {
-    const int kb = i * 64 + lane;
-    const bool valid = kb < n;
+    const bool valid = i * 64 + lane < n;
     const bool is_gt = valid && keys[i] > T;
     const bool is_eq = valid && keys[i] == T;
     const unsigned long long eqb = __ballot(is_eq);
@@ -81,11 +86,83 @@ __device__ __forceinline__ int topk_select_row(const unsigned long long (&keys)[
     const bool take = is_gt || (is_eq && rank < need);
     const unsigned long long tb = __ballot(take);
     const int slot = written + __popcll(tb & lt_mask);
-    if (take && slot < topk) emit(slot, kb);
+    if (take && slot < topk) emit(slot, index_of(i));
     written += __popcll(tb);
     eq_before += __popcll(eqb);
   }
   return written;
+}
+
+template <int MAXG, class Emit>
+__device__ __forceinline__ int topk_select_row(const unsigned long long (&keys)[MAXG], int n, int topk,
+                                               unsigned long long* gather, Emit emit) {
+  const int lane = __lane_id();
+  return topk_core<MAXG>(keys, n, topk, gather, [&](int i) { return i * 64 + lane; }, emit);
+}
+
+
+// The same selection with a pre-filter, for rows of at least 64 candidates and
+// topk <= 64: every lane holds a real candidate and its largest key is >= T0, the
+// smallest of the 64 lane maxima, so at least 64 keys are >= T0 and every kept key
+// (the topk-th largest and above, ties included) is >= T0.  When at most
+// 64 CF keys are >= T0 they are gathered in index order through ck / ci (LDS of
+// this wave, 64 CF entries each) and searched
+// instead of all MAXG groups; otherwise the full search runs.  CF (8 or 16)
+// groups of candidates at most: the search runs over CF/2 groups when they fit,
+// else over CF (a wider search costs registers, so callers with many rows per
+// CU take CF = 8).
+template <int CF, int MAXG, class Emit>
+__device__ __forceinline__ int topk_select_row_filtered(const unsigned long long (&keys)[MAXG], int n, int topk,
+                                                        unsigned long long* gather, unsigned long long* ck,
+                                                        int* ci, Emit emit) {
+  static_assert(CF == 8 || CF == 16, "8 or 16 candidate groups");
+  const int lane = __lane_id();
+  if (MAXG <= CF / 2 || n < 64 || topk > 64) return topk_select_row<MAXG>(keys, n, topk, gather, emit);
+  unsigned long long lm = 0;
+#pragma unroll
+  for (int i = 0; i < MAXG; ++i) lm = keys[i] > lm ? keys[i] : lm;
+  // wave minimum of the lane maxima (64-bit, as two 32-bit halves)
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned lo = __shfl_xor((unsigned)lm, off), hi = __shfl_xor((unsigned)(lm >> 32), off);
+    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+    lm = o < lm ? o : lm;
+  }
+  const unsigned long long t0 = lm;
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < MAXG; ++i) cnt += __popcll(__ballot(keys[i] >= t0));
+  // the narrower search only pays while it has fewer groups than the full one
+  if (cnt > 64 * (CF / 2) && (MAXG <= CF || cnt > 64 * CF)) return topk_select_row<MAXG>(keys, n, topk, gather, emit);
+  const unsigned long long lt_mask = (1ull << lane) - 1ull;
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < MAXG; ++i) {
+    const bool c = keys[i] >= t0;
+    const unsigned long long m = __ballot(c);
+    if (c) {
+      const int pos = base + __popcll(m & lt_mask);
+      ck[pos] = keys[i];
+      ci[pos] = i * 64 + lane;
+    }
+    base += __popcll(m);
+  }
+  __builtin_amdgcn_wave_barrier();
+  auto search = [&](auto groups) {
+    constexpr int NG = decltype(groups)::value;
+    unsigned long long fk[NG];
+    int fi[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const bool in = j * 64 + lane < cnt;
+      fk[j] = in ? ck[j * 64 + lane] : 0ull;
+      fi[j] = in ? ci[j * 64 + lane] : 0;
+    }
+    __builtin_amdgcn_wave_barrier();  // ck / ci are free again once read
+    return topk_core<NG>(fk, cnt, topk, gather, [&](int j) { return fi[j]; }, emit);
+  };
+  if (cnt <= 64 * (CF / 2)) return search(std::integral_constant<int, CF / 2>());
+  return search(std::integral_constant<int, (MAXG > CF ? CF : CF / 2)>());  // MAXG > CF here
 }
 
 }  // namespace hsk
