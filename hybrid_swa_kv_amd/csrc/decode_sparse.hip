@@ -9,8 +9,9 @@
 //  int8_sparse_select_kernel: one workgroup per (sequence, KV head); its four
 //      waves take the group's query heads in turn, load a head's scores as order
 //      keys into registers and run the shared top-k threshold search; every kept
-//      block sets its head's bit in an LDS word per block, and wave 0 then writes
-//      the union of the group's kept blocks in ascending order with those bits.
+//      block sets its head's bit in an LDS word per block, and the four waves
+//      then write the union of the group's kept blocks in ascending order with
+//      those bits, each a quarter of the blocks.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "topk.hpp"
@@ -99,6 +100,7 @@ template <int MAXG>
 __global__ __launch_bounds__(256) void int8_sparse_select_kernel(SparseDecodeArgs a) {
   extern __shared__ unsigned hb[];  // [nblk] head bits
   __shared__ unsigned long long gather[4][64];
+  __shared__ int wcount[4];
   constexpr int CF = 16;  // pre-filtered candidate groups (the slowest row sets this kernel's time)
   __shared__ unsigned long long fck[4][64 * CF];
   __shared__ int fci[4][64 * CF];
@@ -136,24 +138,37 @@ __global__ __launch_bounds__(256) void int8_sparse_select_kernel(SparseDecodeArg
     for (int i = written + lane; i < topk; i += 64) out[i] = -1;
   }
   __syncthreads();
-  if (w != 0) return;
-  // union of the group's kept blocks, ascending, with their head bits
+  // union of the group's kept blocks, ascending, with their head bits: the four
+  // waves take consecutive quarters of the 64-block groups, count their kept
+  // blocks, and write them after the counts of the waves before
+  constexpr int MAXQ = (MAXG + 3) / 4;  // groups per wave (MAXG groups hold nblk)
+  const int per = (((nblk + 63) >> 6) + 3) >> 2;
+  unsigned mm[MAXQ];
+  int mine = 0;
+#pragma unroll
+  for (int q = 0; q < MAXQ; ++q) {
+    const int j = (w * per + q) * 64 + lane;
+    mm[q] = (q < per && j < nblk) ? hb[j] : 0u;
+    mine += __popcll(__ballot(mm[q] != 0u));
+  }
+  if (lane == 0) wcount[w] = mine;
+  __syncthreads();
+  int cnt = 0;
+  for (int i = 0; i < w; ++i) cnt += wcount[i];
   int32_t* ul = a.ulist + (size_t)unit * a.lmax;
   uint32_t* um = a.umask + (size_t)unit * a.lmax;
   const unsigned long long lt = (1ull << lane) - 1ull;
-  int cnt = 0;
-  for (int base = 0; base < nblk; base += 64) {
-    const int j = base + lane;
-    const unsigned m = j < nblk ? hb[j] : 0u;
-    const unsigned long long bal = __ballot(m != 0u);
+#pragma unroll
+  for (int q = 0; q < MAXQ; ++q) {
+    const unsigned long long bal = __ballot(mm[q] != 0u);
     const int pos = cnt + __popcll(bal & lt);
-    if (m != 0u && pos < a.lmax) {
-      ul[pos] = j;
-      um[pos] = m;
+    if (mm[q] != 0u && pos < a.lmax) {
+      ul[pos] = (w * per + q) * 64 + lane;
+      um[pos] = mm[q];
     }
     cnt += __popcll(bal);
   }
-  if (lane == 0) a.ucount[unit] = min(cnt, a.lmax);
+  if (w == 3 && lane == 0) a.ucount[unit] = min(cnt, a.lmax);  // the last wave ends at the total
 }
 
 }  // namespace
