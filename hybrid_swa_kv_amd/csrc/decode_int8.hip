@@ -108,7 +108,7 @@ __global__ __launch_bounds__(DQ_THREADS, 3) void int8_decode_kernel(Int8DecodeAr
 // wave's list entries are read once into lanes and broadcast per step.  Hot
 // splits and split records are as above.
 template <int D>
-__global__ __launch_bounds__(DQ_THREADS) void int8_sparse_decode_kernel(SparseDecodeArgs a) {
+__global__ __launch_bounds__(DQ_THREADS, 3) void int8_sparse_decode_kernel(SparseDecodeArgs a) {
   __shared__ float sm_m[4][16], sm_l[4][16];
   __shared__ __attribute__((aligned(16))) float sm_o[4][16][stash_row<D>()];
 
@@ -145,22 +145,19 @@ __global__ __launch_bounds__(DQ_THREADS) void int8_sparse_decode_kernel(SparseDe
     using Raw = typename DecodeWave<D>::template Raw<true>;
     auto blk = [&](int k) { return __builtin_amdgcn_readlane(myblk, k); };
     auto step = [&](int k, Raw& cur, Raw& ahead) {
-      if (k + 2 < nmine) st.template load<true>(rows, 32 * blk(k + 2), ahead);
+      if (k + 1 < nmine) st.template load<true>(rows, 32 * blk(k + 1), ahead);
       const int j = blk(k);
       st.template compute<true>(rows, 32 * j, cur, ks[j] * a.scale_log2, vs[j],
                                 (unsigned)__builtin_amdgcn_readlane((int)mymask, k));
     };
-    if (nmine > 0) {  // three blocks in flight, as in the dense decode
-      Raw r0, r1, r2;
+    if (nmine > 0) {  // two blocks in flight at three waves per SIMD, as in the dense decode
+      Raw r0, r1;
       st.template load<true>(rows, 32 * blk(0), r0);
-      if (nmine > 1) st.template load<true>(rows, 32 * blk(1), r1);
-      for (int k = 0;; k += 3) {
-        step(k, r0, r2);
+      for (int k = 0;; k += 2) {
+        step(k, r0, r1);
         if (k + 1 >= nmine) break;
         step(k + 1, r1, r0);
         if (k + 2 >= nmine) break;
-        step(k + 2, r2, r1);
-        if (k + 3 >= nmine) break;
       }
     }
   } else {
