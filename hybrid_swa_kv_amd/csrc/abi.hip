@@ -33,7 +33,7 @@ size_t int8_ws_bytes(int B, int Hq, int Hkv, int D, int T8, int Th) {
   return (size_t)B * Hkv * (size_t)nsplit * (size_t)(Hq / Hkv) * (size_t)(D + 2) * sizeof(float);
 }
 
-// block sums [Hq + Hkv][D][nbp] and the score triangle [Hq][nb (nb - 1) / 2], fp64
+// block sums [Hq + Hkv][nbp][D] and the score triangle [Hq][nb (nb - 1) / 2], fp64
 size_t bs_ws_bytes(int L, int Hq, int Hkv, int D, int block) {
   const size_t nb = (size_t)L / block;
   const size_t nbp = (nb + 63) / 64 * 64;

@@ -5,7 +5,8 @@
 //  1. bs_sums:   per 64-token block, fp64 sums of Q (all query heads) and of K.
 //                bf16 values have 8-bit significands, so these sums are exact in
 //                fp64 for the value ranges met here and do not depend on order.
-//                Both are stored d-major, [H][D][nb].
+//                Both are stored block-major, [H][nbp][D]: one thread's 8
+//                consecutive d of a block are 64 contiguous bytes.
 //  2. bs_scores: per query head, the lower triangle of sumQ * sumK^T (fp64) as a
 //                64 x 64-tiled GEMM with 4 x 4 register tiles: each K sum read from
 //                LDS serves 64 query blocks.  score = sumQ . sumK / 4096 orders
@@ -59,9 +60,9 @@ __global__ __launch_bounds__(SUM_THREADS) void bs_sums_kernel(BlockSparseArgs a)
     }
     const int e = vi * 8;
     const int h = e / a.D, d = e % a.D;
-    double* dst = isq ? a.qsum : a.ksum;
+    double* dst = (isq ? a.qsum : a.ksum) + ((size_t)h * a.nbp + blk) * a.D + d;  // block-major
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dst[((size_t)h * a.D + d + j) * a.nbp + blk] = acc[j];
+    for (int j = 0; j < 8; j += 2) *(double2*)(dst + j) = make_double2(acc[j], acc[j + 1]);
   }
 }
 
@@ -78,8 +79,10 @@ constexpr int SC_SLAB = 32;     // d values staged per pass
 // row stride nbp, so a tile never leaves its arrays; entries past nb are never
 // stored.
 __global__ __launch_bounds__(256) void bs_scores_kernel(BlockSparseArgs a) {
-  __shared__ __attribute__((aligned(16))) double sq[SC_SLAB][SC_TILE];
-  __shared__ __attribute__((aligned(16))) double sk[SC_SLAB][SC_TILE];
+  // d-major slabs; rows padded by two doubles (rows stay 16-byte aligned) to
+  // spread the transposing writes over the banks
+  __shared__ __attribute__((aligned(16))) double sq[SC_SLAB][SC_TILE + 2];
+  __shared__ __attribute__((aligned(16))) double sk[SC_SLAB][SC_TILE + 2];
   const int T = a.nbp / SC_TILE;
   const int ntri = T * (T + 1) / 2;
   const int h = blockIdx.x / ntri;
@@ -89,21 +92,26 @@ __global__ __launch_bounds__(256) void bs_scores_kernel(BlockSparseArgs a) {
   const int tj = r - ti * (ti + 1) / 2;
   const int g = h / (a.Hq / a.Hkv);
   const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
-  const double* qsrc = a.qsum + (size_t)h * a.D * a.nbp + ti * SC_TILE;
-  const double* ksrc = a.ksum + (size_t)g * a.D * a.nbp + tj * SC_TILE;
+  const double* qsrc = a.qsum + ((size_t)h * a.nbp + ti * SC_TILE) * a.D;  // block-major sums
+  const double* ksrc = a.ksum + ((size_t)g * a.nbp + tj * SC_TILE) * a.D;
   double acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
   for (int d0 = 0; d0 < a.D; d0 += SC_SLAB) {
-    // stage 32 d x 64 blocks of each operand: 4 x 16 bytes per thread per operand
+    // stage 64 blocks x 32 d of each operand (a block's 32 d are 256 contiguous
+    // bytes): 4 x 16 bytes per thread per operand, transposed into the d-major slabs
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int u = i * 256 + t;  // 16-byte unit: d row u / 32, block pair u % 32
-      const int dd = u >> 5, c = (u & 31) * 2;
-      *(double2*)&sq[dd][c] = *(const double2*)(qsrc + (size_t)(d0 + dd) * a.nbp + c);
-      *(double2*)&sk[dd][c] = *(const double2*)(ksrc + (size_t)(d0 + dd) * a.nbp + c);
+      const int u = i * 256 + t;  // 16-byte unit: block u / 16, d pair u % 16
+      const int c = u >> 4, dd = (u & 15) * 2;
+      const double2 qv = *(const double2*)(qsrc + (size_t)c * a.D + d0 + dd);
+      const double2 kv = *(const double2*)(ksrc + (size_t)c * a.D + d0 + dd);
+      sq[dd][c] = qv.x;
+      sq[dd + 1][c] = qv.y;
+      sk[dd][c] = kv.x;
+      sk[dd + 1][c] = kv.y;
     }
     __syncthreads();
 #pragma unroll 8

@@ -80,8 +80,8 @@ struct BlockSparseArgs {
   const uint16_t* v;
   uint16_t* out;      // [L, Hq, D]
   int32_t* sel;       // [Hq, nb, topk]
-  double* qsum;       // [Hq, D, nbp] block sums of Q (columns past nb unused)
-  double* ksum;       // [Hkv, D, nbp] block sums of K
+  double* qsum;       // [Hq, nbp, D] block sums of Q (blocks past nb unused)
+  double* ksum;       // [Hkv, nbp, D] block sums of K
   double* scores;     // [Hq][nb (nb - 1) / 2] packed lower triangle of sumQ . sumK
   int L, Hq, Hkv, D, block, topk, window, nb;
   int nbp;            // nb rounded up to a multiple of 64
