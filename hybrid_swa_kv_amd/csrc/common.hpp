@@ -55,6 +55,13 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16x16x16 bf16 -> fp32.  Lane l: A[m = l%16][k = 4(l/16)+j], B[k = 4(l/16)+j][n = l%16],
+// C/D as for the 16x16x32 form.
+__device__ __forceinline__ f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                   0, 0, 0);
+}
+
 // ------------------------------------------------------- lane exchanges ----
 // value held by lane l ^ 32 (v_permlane32_swap).
 __device__ __forceinline__ float xor32(float x) {

@@ -129,7 +129,7 @@ struct DecodeWave {
   // One chunk of 16 NT rows c0 .. c0+16 NT-1 of `rows` (NT = 1 or 2 blocks of 16
   // keys; see the row sources below).  sk multiplies the raw scores (scale *
   // log2 e, times the K scale for INT8), sv multiplies the chunk's PV partial
-  // (the V scale for INT8, else 1).
+  // (the V scale; INT8 only: bf16 rows accumulate PV in place, sv is ignored).
   template <bool INT8, int NT = 2, class Rows>
   __device__ __forceinline__ void chunk(const Rows& rows, int c0, float sk, float sv) {
     Raw<INT8> raw;
@@ -275,12 +275,12 @@ struct DecodeWave {
         }
       }
     }
-    bf16x8 va[NK][4];
+    u32x4 va[NK][4];
 #pragma unroll
     for (int hv = 0; hv < NK; ++hv) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        u32x4 t;
+        u32x4& t = va[hv][jj];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           if (2 * q >= 4 * NT) {  // key slots past the chunk: zero
@@ -295,7 +295,6 @@ struct DecodeWave {
                             : __builtin_amdgcn_perm(x1, x0, 0x05040100u);
           }
         }
-        va[hv][jj] = as_bf16x8(t);
       }
     }
     float x[8];
@@ -348,21 +347,46 @@ struct DecodeWave {
       ps += bf16lo(pw[q]) + bf16hi(pw[q]);
     }
     l += ps;
-    const bf16x8 pb = as_bf16x8(pw);
+    if constexpr (INT8) {  // the chunk's partial, scaled by its V scale
+      const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
-    for (int hv = 0; hv < NK; ++hv)
+      for (int hv = 0; hv < NK; ++hv)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        f32x4 part = {0.f, 0.f, 0.f, 0.f};
-        part = mfma16(va[hv][jj], pb, part);
+        for (int jj = 0; jj < 4; ++jj) {
+          f32x4 part = {0.f, 0.f, 0.f, 0.f};
+          part = mfma16(as_bf16x8(va[hv][jj]), pb, part);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[hv][jj][r] = fmaf(sv, part[r], o[hv][jj][r]);
-      }
+          for (int r = 0; r < 4; ++r) o[hv][jj][r] = fmaf(sv, part[r], o[hv][jj][r]);
+        }
+    } else if constexpr (NT == 1) {
+      // one key block: its 16 keys are exactly the 16-deep form's contraction
+      // (lane group g holds keys 4g..4g+3 in both operands), so the zero half
+      // of the 32-deep operands is not formed; bf16 rows accumulate in place
+      const u32x2 pb = {pw[0], pw[1]};
+#pragma unroll
+      for (int hv = 0; hv < NK; ++hv)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const u32x2 v2 = {va[hv][jj][0], va[hv][jj][1]};
+          o[hv][jj] = mfma16k16(v2, pb, o[hv][jj]);
+        }
+    } else {
+      const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+      for (int hv = 0; hv < NK; ++hv)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) o[hv][jj] = mfma16(as_bf16x8(va[hv][jj]), pb, o[hv][jj]);
+    }
   }
 
   // Write this wave's state for the heads it serves (lane%16 < G) to LDS:
-  // sm_m/sm_l [waves][16], sm_o [waves][16][stash_row<D>()]; a lane's four
-  // jj values of one (hv, r) are adjacent columns, stored as one 128-bit write.
+  // sm_m/sm_l [waves][16], sm_o [waves][16][stash_row<D>()].  A head's row holds
+  // its D accumulators in tile order: tile (hv, jj) of lane group g is one
+  // 128-bit write at column 64 hv + 16 jj + 4 g (its four registers r are
+  // d = 64 hv + 16 g + 4 r + jj); stash_col maps d to its column.
+  __device__ __forceinline__ static int stash_col(int d) {
+    return (d & ~63) + 16 * (d & 3) + 4 * ((d >> 4) & 3) + ((d >> 2) & 3);
+  }
   __device__ __forceinline__ void stash(float (*sm_m)[16], float (*sm_l)[16], float (*sm_o)[16][stash_row<D>()],
                                         int w, int G) {
     const int lane = __lane_id();
@@ -374,9 +398,8 @@ struct DecodeWave {
 #pragma unroll
       for (int hv = 0; hv < NK; ++hv)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          *(float4*)&sm_o[w][hl][64 * hv + 16 * gq + 4 * r] =
-              make_float4(o[hv][0][r], o[hv][1][r], o[hv][2][r], o[hv][3][r]);
+        for (int jj = 0; jj < 4; ++jj)
+          *(f32x4*)&sm_o[w][hl][64 * hv + 16 * jj + 4 * gq] = o[hv][jj];
       if (gq == 0) {
         sm_m[w][hl] = m;
         sm_l[w][hl] = lsum;
@@ -390,6 +413,7 @@ template <int NW, int D>
 __device__ __forceinline__ float merge_waves(const float (*sm_m)[16], const float (*sm_l)[16],
                                              const float (*sm_o)[16][stash_row<D>()], int head, int d,
                                              float& M, float& Ls) {
+  const int col = DecodeWave<D>::stash_col(d);
   M = kNegInf;
 #pragma unroll
   for (int i = 0; i < NW; ++i) M = fmaxf(M, sm_m[i][head]);
@@ -398,7 +422,32 @@ __device__ __forceinline__ float merge_waves(const float (*sm_m)[16], const floa
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
     const float f = (sm_m[i][head] == kNegInf) ? 0.f : fast_exp2(sm_m[i][head] - M);
-    O += f * sm_o[i][head][d];
+    O += f * sm_o[i][head][col];
+    Ls += f * sm_l[i][head];
+  }
+  return O;
+}
+
+// Merge NW stashed wave states for the four columns col .. col+3 (col a
+// multiple of 4) of a head's row: returns the four accumulators, sets M and
+// Lsum (the wave factors are formed once for the four).
+template <int NW, int D>
+__device__ __forceinline__ f32x4 merge_waves4(const float (*sm_m)[16], const float (*sm_l)[16],
+                                              const float (*sm_o)[16][stash_row<D>()], int head, int col,
+                                              float& M, float& Ls) {
+  M = kNegInf;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) M = fmaxf(M, sm_m[i][head]);
+  f32x4 O = {0.f, 0.f, 0.f, 0.f};
+  Ls = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const float f = (sm_m[i][head] == kNegInf) ? 0.f : fast_exp2(sm_m[i][head] - M);
+    const float4 v = *(const float4*)&sm_o[i][head][col];
+    O[0] += f * v.x;
+    O[1] += f * v.y;
+    O[2] += f * v.z;
+    O[3] += f * v.w;
     Ls += f * sm_l[i][head];
   }
   return O;

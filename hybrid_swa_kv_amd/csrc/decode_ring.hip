@@ -25,11 +25,19 @@ constexpr int RD_THREADS = 64 * RD_WAVES;
 constexpr int RD_CHUNK = 16;                     // slots per wave per step
 constexpr int RD_STRIDE = RD_CHUNK * RD_WAVES;   // slots per workgroup step
 
+// One LDS object, the small per-wave (max, sum) arrays first, so the merge
+// addresses them with immediate offsets.
+template <int D>
+struct RingShared {
+  float m[RD_WAVES][16], l[RD_WAVES][16];
+  float o[RD_WAVES][16][stash_row<D>()];
+  uint16_t in[(16 + 2) * D];
+};
+
 template <int D>
 __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs a) {
-  __shared__ float sm_m[RD_WAVES][16], sm_l[RD_WAVES][16];
-  __shared__ __attribute__((aligned(16))) float sm_o[RD_WAVES][16][stash_row<D>()];
-  __shared__ __attribute__((aligned(16))) uint16_t sm_in[(16 + 2) * D];
+  __shared__ __attribute__((aligned(16))) RingShared<D> sh;
+  uint16_t* const sm_in = sh.in;
 
   const int G = a.Hq / a.Hkv;
   const int HG = G < 16 ? G : 16;  // heads served by this workgroup
@@ -96,13 +104,20 @@ __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs 
   }
   if (c0 < W) st.template compute<false, 1>(rows, c0, cur, a.scale_log2, 1.f, alt, ~0u, c0 == first);
 
-  st.stash(sm_m, sm_l, sm_o, w, HG);
+  st.stash(sh.m, sh.l, sh.o, w, HG);
   __syncthreads();
-  for (int e = t; e < HG * D; e += RD_THREADS) {
-    const int head = e / D, d = e % D;
+  // One stashed tile (four columns) per thread, so the waves' factors are formed
+  // once for four outputs; its outputs are d = base + 4 r.  Thread order runs
+  // over jj fastest, so four lanes' stores of one r cover 8 contiguous bytes.
+  for (int e = t; e < HG * D / 4; e += RD_THREADS) {
+    const int head = e / (D / 4), q = e % (D / 4);
+    const int hv = q >> 4, gq = (q >> 2) & 3, jj = q & 3;
     float M, Ls;
-    const float O = merge_waves<RD_WAVES, D>(sm_m, sm_l, sm_o, head, d, M, Ls);
-    a.out[((size_t)b * a.Hq + h0 + head) * D + d] = f32_to_bf16(ok ? O * __builtin_amdgcn_rcpf(Ls) : 0.f);
+    const f32x4 O = merge_waves4<RD_WAVES, D>(sh.m, sh.l, sh.o, head, 64 * hv + 16 * jj + 4 * gq, M, Ls);
+    const float rl = __builtin_amdgcn_rcpf(Ls);
+    uint16_t* dst = a.out + ((size_t)b * a.Hq + h0 + head) * D + 64 * hv + 16 * gq + jj;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[4 * r] = f32_to_bf16(ok ? O[r] * rl : 0.f);
   }
 }
 
