@@ -24,6 +24,7 @@ constexpr int RD_WAVES = 8;
 constexpr int RD_THREADS = 64 * RD_WAVES;
 constexpr int RD_CHUNK = 16;                     // slots per wave per step
 constexpr int RD_STRIDE = RD_CHUNK * RD_WAVES;   // slots per workgroup step
+constexpr int RD_NT = RD_CHUNK / 16;             // 16-key MFMA blocks per chunk
 
 // One LDS object, the small per-wave (max, sum) arrays first, so the merge
 // addresses them with immediate offsets.
@@ -60,13 +61,18 @@ __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs 
   const uint16_t* vn = a.v_new + kvoff * D;
   // q of the served heads and the new token's K and V rows are staged once per
   // workgroup in LDS (sm_in: HG*D q values, then D of k_new, then D of v_new):
-  // each thread fetches one 16-byte piece, issued before its ring loads so the
-  // wait for it does not wait for the ring data.
+  // each thread fetches up to RD_PIECES 16-byte pieces, issued before its ring
+  // loads so the wait for them does not wait for the ring data.
   const int nq = HG * D / 8, nin = nq + D / 4;
-  const int pi = min(t, nin - 1);
-  const uint16_t* src = pi < nq ? a.q + ((size_t)b * a.Hq + h0) * D + 8 * pi
-                        : pi < nq + D / 8 ? kn + 8 * (pi - nq) : vn + 8 * (pi - nq - D / 8);
-  const uint4 piece = *(const uint4*)src;
+  constexpr int RD_PIECES = ((16 + 2) * D / 8 + RD_THREADS - 1) / RD_THREADS;
+  uint4 piece[RD_PIECES];
+#pragma unroll
+  for (int i = 0; i < RD_PIECES; ++i) {
+    const int pi = min(t + i * RD_THREADS, nin - 1);
+    const uint16_t* src = pi < nq ? a.q + ((size_t)b * a.Hq + h0) * D + 8 * pi
+                          : pi < nq + D / 8 ? kn + 8 * (pi - nq) : vn + 8 * (pi - nq - D / 8);
+    piece[i] = *(const uint4*)src;
+  }
   __builtin_amdgcn_sched_barrier(0);
   DecodeWave<D, true> st;
   RingRows<D> rows{rk, rv, sm_in + HG * D, sm_in + HG * D + D, W, 0, -1};
@@ -74,14 +80,16 @@ __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs 
   using Raw = typename DecodeWave<D, true>::template Raw<false>;
   Raw cur, nxt;
   const int first = RD_CHUNK * w;
-  st.template load<false, 1>(rows, first, cur);
+  st.template load<false, RD_NT>(rows, first, cur);
   __builtin_amdgcn_sched_barrier(0);  // keep the pos load and its use behind the chunk loads
   const int p = a.pos[b];
   const bool ok = p >= 0;
   const int slot = (int)((unsigned)max(p, 0) % (unsigned)W);  // branch-free
   rows.slot = slot;
   rows.p = ok ? p : -1;
-  if (t < nin) *(uint4*)(sm_in + 8 * t) = piece;
+#pragma unroll
+  for (int i = 0; i < RD_PIECES; ++i)
+    if (t + i * RD_THREADS < nin) *(uint4*)(sm_in + 8 * (t + i * RD_THREADS)) = piece[i];
   __syncthreads();
   // append: the first head group's workgroup writes the new token into its slot
   // now, so the stores complete while the ring loads are in flight.  Any read of
@@ -97,12 +105,12 @@ __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs 
   st.load_alt(rows, alt);
   int c0 = first;
   for (; c0 + RD_STRIDE < W; c0 += 2 * RD_STRIDE) {
-    st.template load<false, 1>(rows, c0 + RD_STRIDE, nxt);
-    st.template compute<false, 1>(rows, c0, cur, a.scale_log2, 1.f, alt, ~0u, c0 == first);
-    if (c0 + 2 * RD_STRIDE < W) st.template load<false, 1>(rows, c0 + 2 * RD_STRIDE, cur);
-    st.template compute<false, 1>(rows, c0 + RD_STRIDE, nxt, a.scale_log2, 1.f, alt);
+    st.template load<false, RD_NT>(rows, c0 + RD_STRIDE, nxt);
+    st.template compute<false, RD_NT>(rows, c0, cur, a.scale_log2, 1.f, alt, ~0u, c0 == first);
+    if (c0 + 2 * RD_STRIDE < W) st.template load<false, RD_NT>(rows, c0 + 2 * RD_STRIDE, cur);
+    st.template compute<false, RD_NT>(rows, c0 + RD_STRIDE, nxt, a.scale_log2, 1.f, alt);
   }
-  if (c0 < W) st.template compute<false, 1>(rows, c0, cur, a.scale_log2, 1.f, alt, ~0u, c0 == first);
+  if (c0 < W) st.template compute<false, RD_NT>(rows, c0, cur, a.scale_log2, 1.f, alt, ~0u, c0 == first);
 
   st.stash(sh.m, sh.l, sh.o, w, HG);
   __syncthreads();

@@ -20,6 +20,7 @@
 namespace hsk {
 
 constexpr int FT_BN = 64;  // keys per tile
+constexpr int FT_KPF = 4;  // K fragments read ahead
 
 template <int D>
 struct FtCfg {
@@ -171,15 +172,26 @@ struct FlashWave {
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[sub][r] = 0.f;
-    // the two key blocks are independent accumulation chains: alternate them
+    // the two key blocks are independent accumulation chains: alternate them.
+    // K fragments are read FT_KPF steps ahead of their MFMA (a rolling window of
+    // registers), so LDS latency hides behind the MFMAs in between; the
+    // scheduling barriers keep the compiler from regrouping the reads next to
+    // their MFMAs (its own order waited for a read before nearly every MFMA).
+    constexpr int NS = 2 * C::DC;
+    bf16x8 kb[FT_KPF];
+    auto kread = [&](int i) {  // step i: key block i % 2, k-step i / 2
+      return *(const bf16x8*)(ks + 32 * (i & 1) * C::NCH * 16 + ko[i >> 1]);
+    };
 #pragma unroll
-    for (int c = 0; c < C::DC; ++c)
+    for (int i = 0; i < FT_KPF; ++i) kb[i] = kread(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        // key 32 sub + lane%32, chunk 2c + lane/32
-        const bf16x8 ka = *(const bf16x8*)(ks + 32 * sub * C::NCH * 16 + ko[c]);
-        s[sub] = mfma32(ka, qf[c], s[sub]);
-      }
+    for (int i = 0; i < NS; ++i) {
+      const bf16x8 ka = kb[i % FT_KPF];
+      if (i + FT_KPF < NS) kb[i % FT_KPF] = kread(i + FT_KPF);
+      s[i & 1] = mfma32(ka, qf[i >> 1], s[i & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // Online softmax of one tile's scores (masked when `mask`; k0: first key of the
