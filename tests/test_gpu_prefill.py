@@ -44,7 +44,7 @@ CASES = [
     (1, 2, 2, 128, 128), (2, 4, 1, 128, 1), (63, 2, 2, 64, 0), (64, 4, 1, 128, 64),
     (65, 8, 2, 128, 64), (127, 2, 2, 128, 127), (128, 4, 2, 64, 128), (129, 8, 2, 128, 129),
     (300, 4, 4, 128, 1), (513, 8, 2, 128, 100), (1000, 8, 2, 128, 0), (1000, 4, 1, 64, 256),
-    (777, 16, 2, 128, 1024), (2048, 8, 1, 128, 333),
+    (777, 16, 2, 128, 1024), (2048, 8, 1, 128, 333), (259, 3, 1, 128, 70), (190, 6, 2, 64, 0),
 ]
 
 
