@@ -257,6 +257,15 @@ class Timer:
         ev = self.ms[name][skip:]
         return sum(a.elapsed_time(b) for a, b in ev) / max(1, len(ev))
 
+    def spread(self, name, skip=0, per=1):
+        """median, min and p90 of the timed calls of a row (ms, divided by `per`)."""
+        v = sorted(a.elapsed_time(b) / per for a, b in self.ms[name][skip:])
+        if not v:
+            return None
+        p90 = v[min(len(v) - 1, int(0.9 * (len(v) - 1) + 0.5))]
+        return {"median_ms": round(v[len(v) // 2], 5), "min_ms": round(v[0], 5), "p90_ms": round(p90, 5),
+                "calls": len(v)}
+
 
 def cpu_baseline(target_s: float):
     """The oracle on a bounded sample of the ring-decode workload (one thread)."""
@@ -300,8 +309,8 @@ def cpu_baseline(target_s: float):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--rows", default="ring,int8,int8sparse,quant,swa,full,chunk4096,chunk8192,sparse,hybrid70")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -604,6 +613,11 @@ def main() -> int:
     for name, st in sclk.items():
         if name in res and isinstance(res[name], dict):
             res[name]["sclk_mhz"] = st
+    # spread of the timed calls (per launch for the ring row, whose step is 60 launches)
+    for name in rows:
+        if name in res and isinstance(res[name], dict):
+            per = RING["layers"] if name == "ring" else 1
+            res[name]["per_launch_ms" if name == "ring" else "call_ms"] = timer.spread(name, args.warmup, per)
 
     line = {
         "metric": METRIC,
