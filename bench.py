@@ -643,6 +643,11 @@ def main() -> int:
                             "achieved": res["ring"]["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": res["ring"]["frac_hbm_peak"], "traffic": recorded_traffic()}
     line["rows"] = res
+    props = torch.cuda.get_device_properties(0)
+    line["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                      "compute_units": props.multi_processor_count,
+                      "peaks_used": {"bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS,
+                                     "basis": "256 CUs x 2.4 GHz x 4096 bf16 FLOP/clk; 8 TB/s HBM3E"}}
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
