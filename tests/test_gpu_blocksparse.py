@@ -32,7 +32,8 @@ def check_selection(sel_gpu, q, k, block, topk, heads=None):
 
 @pytest.mark.parametrize("L,Hq,Hkv,D,topk,window", [
     (1024, 4, 1, 128, 4, 100), (2048, 8, 2, 128, 8, 1024), (4096, 4, 1, 64, 64, 1024),
-    (1024, 2, 2, 128, 0, 64), (640, 4, 2, 128, 256, 64), (2048, 4, 1, 128, 3, 4096)])
+    (1024, 2, 2, 128, 0, 64), (640, 4, 2, 128, 256, 64), (2048, 4, 1, 128, 3, 4096),
+    (8192, 32, 8, 128, 64, 1024)])  # the 131072-token workload's heads, blocks, top-k and window at L 8192
 def test_blocksparse_parity(L, Hq, Hkv, D, topk, window):
     announce("blocksparse", L=L, Hq=Hq, Hkv=Hkv, D=D, topk=topk, window=window)
     seed = 90 + L + topk

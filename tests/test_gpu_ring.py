@@ -57,7 +57,7 @@ def run_case(seed, B, Hq, Hkv, D, W, pos):
     assert ex <= 0, (ex, max_abs(out_f64(out), ref))
 
 
-@pytest.mark.parametrize("W", [1, 16, 128, 200])
+@pytest.mark.parametrize("W", [1, 16, 128, 200, 640, 1024])
 def test_ring_positions(W):
     B = 7
     pos = [0, 1, max(0, W - 2), W - 1, W, W + 1, 12345]
