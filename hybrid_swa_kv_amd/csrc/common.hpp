@@ -17,7 +17,6 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // ---------------------------------------------------------------- bf16 ----
@@ -103,13 +102,6 @@ __device__ __forceinline__ float row16_max(float x) {
   x = fmaxf(x, dpp<kDppXor2>(x));
   x = fmaxf(x, dpp<kDppHalfMirror>(x));
   x = fmaxf(x, dpp<kDppMirror>(x));
-  return x;
-}
-// sum / max over each aligned group of 8 lanes
-__device__ __forceinline__ float row8_sum(float x) {
-  x += dpp<kDppXor1>(x);
-  x += dpp<kDppXor2>(x);
-  x += dpp<kDppHalfMirror>(x);
   return x;
 }
 

@@ -43,7 +43,6 @@ __device__ __forceinline__ void cvt16(uint4 c, bf16x8& lo, bf16x8& hi) {
 // that a load is filling makes the compiler wait for that load right away, so
 // masking is done with bit operations on the loaded value instead.
 __device__ __forceinline__ unsigned lane_mask(bool c) { return c ? 0xffffffffu : 0u; }
-__device__ __forceinline__ uint4 and4(uint4 a, unsigned m) { return make_uint4(a.x & m, a.y & m, a.z & m, a.w & m); }
 __device__ __forceinline__ uint2 and2(uint2 a, unsigned m) { return make_uint2(a.x & m, a.y & m); }
 __device__ __forceinline__ uint4 sel4(uint4 a, uint4 b, unsigned m) {  // m ? a : b
   return make_uint4((a.x & m) | (b.x & ~m), (a.y & m) | (b.y & ~m), (a.z & m) | (b.z & ~m), (a.w & m) | (b.w & ~m));
