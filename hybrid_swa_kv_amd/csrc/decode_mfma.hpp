@@ -166,14 +166,24 @@ struct DecodeWave {
               rows.rv, vl + (16 * (j >> 2) + (j & 3)) * D + 64 * hv, soff, 0);
       return;
     }
+    // Rows::kStream: the rows are read once per call and are too large to stay
+    // cached, so they are loaded non-temporally (measured faster for long bf16
+    // contexts, slower for the latency-bound 128-slot ring)
+    auto ld4 = [](const char* p) {
+      if constexpr (Rows::kStream) return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)p));
+      else return *(const uint4*)p;
+    };
+    auto ld2 = [](const char* p) {
+      if constexpr (Rows::kStream) return __builtin_bit_cast(uint2, __builtin_nontemporal_load((const u32x2*)p));
+      else return *(const uint2*)p;
+    };
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const char* kp = (const char*)rows.kaddr(c0 + 16 * t + hl);
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
-        for (int e = 0; e < KV; ++e)
-          raw.k[t][kk][e] = *(const uint4*)(kp + (INT8 ? 64 * kk + 16 * gq : 2 * qk_col(kk, e, gq)));
+        for (int e = 0; e < KV; ++e) raw.k[t][kk][e] = ld4(kp + (INT8 ? 64 * kk + 16 * gq : 2 * qk_col(kk, e, gq)));
     }
 #pragma unroll
     for (int hv = 0; hv < NK; ++hv)
@@ -181,7 +191,7 @@ struct DecodeWave {
       for (int j = 0; j < 4 * NT; ++j) {
         const char* vp = (const char*)rows.vaddr(c0 + 16 * (j >> 2) + 4 * gq + (j & 3));
         if (INT8) raw.v8[hv][j] = *(const unsigned*)(vp + 64 * hv + 4 * hl);
-        else raw.v16[hv][j] = *(const uint2*)(vp + 2 * (64 * hv + 4 * hl));
+        else raw.v16[hv][j] = ld2(vp + 2 * (64 * hv + 4 * hl));
       }
   }
 
@@ -463,6 +473,7 @@ struct Int8Rows {
   static constexpr bool kAllValid = true;
   static constexpr bool kHasAlt = false;
   static constexpr bool kBuffer = true;  // loaded through rk / rv
+  static constexpr bool kStream = false;
   const int8_t* k;
   const int8_t* v;
   __amdgpu_buffer_rsrc_t rk, rv;       // the same rows as buffer resources
@@ -482,6 +493,7 @@ struct Bf16Rows {
   static constexpr bool kAllValid = false;
   static constexpr bool kHasAlt = false;
   static constexpr bool kBuffer = false;
+  static constexpr bool kStream = true;
   const uint16_t* k;
   const uint16_t* v;
   int end;
@@ -503,6 +515,7 @@ struct RingRows {
   static constexpr bool kAllValid = false;
   static constexpr bool kHasAlt = true;
   static constexpr bool kBuffer = false;
+  static constexpr bool kStream = false;
   const uint16_t* k;
   const uint16_t* v;
   const void* kalt;
