@@ -439,25 +439,34 @@ __device__ __forceinline__ float merge_waves(const float (*sm_m)[16], const floa
 
 // Merge NW stashed wave states for the four columns col .. col+3 (col a
 // multiple of 4) of a head's row: returns the four accumulators, sets M and
-// Lsum (the wave factors are formed once for the four).
+// Lsum (the wave factors are formed once for the four).  Every LDS read is
+// issued before the arithmetic, so the merge waits for LDS once.
 template <int NW, int D>
 __device__ __forceinline__ f32x4 merge_waves4(const float (*sm_m)[16], const float (*sm_l)[16],
                                               const float (*sm_o)[16][stash_row<D>()], int head, int col,
                                               float& M, float& Ls) {
+  float mv[NW], lv[NW];
+  float4 ov[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    mv[i] = sm_m[i][head];
+    lv[i] = sm_l[i][head];
+    ov[i] = *(const float4*)&sm_o[i][head][col];
+  }
+  __builtin_amdgcn_sched_barrier(0);
   M = kNegInf;
 #pragma unroll
-  for (int i = 0; i < NW; ++i) M = fmaxf(M, sm_m[i][head]);
+  for (int i = 0; i < NW; ++i) M = fmaxf(M, mv[i]);
   f32x4 O = {0.f, 0.f, 0.f, 0.f};
   Ls = 0.f;
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
-    const float f = (sm_m[i][head] == kNegInf) ? 0.f : fast_exp2(sm_m[i][head] - M);
-    const float4 v = *(const float4*)&sm_o[i][head][col];
-    O[0] += f * v.x;
-    O[1] += f * v.y;
-    O[2] += f * v.z;
-    O[3] += f * v.w;
-    Ls += f * sm_l[i][head];
+    const float f = (mv[i] == kNegInf) ? 0.f : fast_exp2(mv[i] - M);
+    O[0] += f * ov[i].x;
+    O[1] += f * ov[i].y;
+    O[2] += f * ov[i].z;
+    O[3] += f * ov[i].w;
+    Ls += f * lv[i];
   }
   return O;
 }
