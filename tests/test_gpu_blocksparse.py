@@ -72,6 +72,28 @@ def test_blocksparse_past_2048_blocks():
     assert ex <= 0, (ex, max_abs(got, ref))
 
 
+
+@pytest.mark.parametrize("topk", [100, 256])
+def test_blocksparse_topk_above_64(topk):
+    """640 key blocks with topk 100 and 256 (the limit): rows choose among more
+    candidates than topk through the unfiltered search; every selection checked,
+    attention on sampled rows on both sides of qb = topk."""
+    L, Hq, Hkv, D, window = 64 * 640, 2, 1, 64, 64
+    announce("blocksparse_topk_above_64", L=L, topk=topk)
+    q = synth.token_major(311 + topk, synth.Q, L, Hq, D)
+    k = synth.token_major(311 + topk, synth.K, L, Hkv, D)
+    v = synth.token_major(311 + topk, synth.V, L, Hkv, D)
+    out, sel = hsk.blocksparse_select_attend(gpu_bf16(q), gpu_bf16(k), gpu_bf16(v), 64, topk, window)
+    sel_np = sel.cpu().numpy()
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    check_selection(sel_np, qf, kf, 64, topk)
+    assert (sel_np[:, topk + 1:] >= 0).all()  # past qb = topk every row keeps exactly topk blocks
+    rows = np.array([0, 64 * topk - 1, 64 * topk, 64 * topk + 64, 64 * topk + 127, 30000, L - 1], dtype=np.int64)
+    got = out_f64(out)[rows]
+    ref = oracle.blocksparse_attend(qf, kf, vf, sel_np, 64, window, rows=rows)
+    ex = bf16_excess(got, ref)
+    assert ex <= 0, (ex, max_abs(got, ref))
+
 def test_blocksparse_exact_tie():
     # duplicate key blocks produce exactly equal scores: the lower block must win
     L, Hq, Hkv, D, topk = 1024, 2, 1, 128, 2

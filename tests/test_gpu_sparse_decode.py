@@ -60,6 +60,8 @@ def check_rows(sel_gpu, scores, topk, rows):
     (2, 8, 2, 128, 0, 70, 16),         # no INT8 region
     (1, 8, 2, 128, 131072, 32, 64),    # 4096 blocks
     (1, 8, 1, 128, 22400, 64, 16),     # 700 blocks, 8 heads per group
+    (1, 8, 2, 128, 32768, 64, 256),    # topk at its limit, 1024 blocks to choose from
+    (2, 8, 2, 64, 12800, 40, 100),     # topk above 64, 400 blocks
 ])
 def test_sparse_decode_parity(B, Hq, Hkv, D, T8, Th, topk):
     announce("sparse_decode", B=B, Hq=Hq, Hkv=Hkv, D=D, T8=T8, Th=Th, topk=topk)
