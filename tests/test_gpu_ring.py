@@ -82,3 +82,10 @@ def test_ring_decode_workload():
     # batch 32, context 32768 (query at position 32767), 32/8 heads, head_dim 128, window 128
     announce("ring_workload")
     run_case(2, 32, 32, 8, 128, 128, [32767] * 32)
+
+
+def test_ring_window_limit():
+    """W = 65536, the largest ring: a fresh sequence, one that fills the ring
+    exactly and one that has wrapped."""
+    announce("ring_W65536")
+    run_case(43, 3, 4, 1, 64, 65536, [0, 65535, 70000])
