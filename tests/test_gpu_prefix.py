@@ -74,3 +74,17 @@ def test_window_safe_len_empty_batch():
     sp = torch.empty((0, 16), dtype=torch.int32, device="cuda")
     ml = torch.empty((0,), dtype=torch.int32, device="cuda")
     assert hsk.swa_window_safe_len(sp, ml).numel() == 0
+
+
+def test_window_safe_len_window_limit():
+    """W = 65536, the largest window: a wrapped ring matched in full, one token
+    short (its window lost a position), one token past the pool, and a ring that
+    has not filled yet."""
+    announce("window_safe W=65536")
+    W, ctx = 65536, 70000
+    pos = np.stack([oracle.ring_positions(ctx - 1, W)] * 3 + [oracle.ring_positions(999, W)]).astype(np.int32)
+    M = np.array([ctx, ctx - 1, ctx + 1, 1000], dtype=np.int32)
+    want = oracle.window_safe_len(pos, M, W)
+    got = _run(pos, M)
+    assert np.array_equal(got.astype(np.int64), want)
+    assert list(want) == [ctx, 0, ctx, 1000]
