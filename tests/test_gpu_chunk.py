@@ -81,3 +81,22 @@ def test_chunks_of_8192_rows_sampled():
     got = out_f64(out)[:, rows]
     ex = bf16_excess(got, ref)
     assert ex <= 0, (ex, max_abs(got, ref))
+
+
+def test_chunked_prefill_window_limit():
+    """W = 65536, longer than the sequence: every chunk reads the whole earlier
+    prefix from the ring (full causal attention); slots past the sequence keep
+    their garbage, written by no chunk and read by none."""
+    L, C, W, Hq, Hkv, D = 1636, 512, 65536, 8, 2, 128
+    announce("prefill_chunk_W65536", L=L, C=C, W=W)
+    B = 2
+    q, k, v, out, rk, rv = _run_chunks(870, B, L, C, Hq, Hkv, D, W)
+    ref = oracle.swa_prefill(f64(q), f64(k), f64(v), W)
+    ex = bf16_excess(out_f64(out), ref)
+    assert ex <= 0, (ex, max_abs(out_f64(out), ref))
+    got_k, got_v = rk.view(torch.int16).cpu().numpy(), rv.view(torch.int16).cpu().numpy()
+    assert np.array_equal(got_k[:, :, :L].view(np.uint16), np.ascontiguousarray(k.transpose(0, 2, 1, 3)))
+    assert np.array_equal(got_v[:, :, :L].view(np.uint16), np.ascontiguousarray(v.transpose(0, 2, 1, 3)))
+    assert np.array_equal(got_k[:, :, L:].view(np.uint16), synth.head_major(870, synth.MISC, B, Hkv, W, D)[:, :, L:])
+    assert np.array_equal(got_v[:, :, L:].view(np.uint16),
+                          synth.head_major(870, synth.MISC + 1, B, Hkv, W, D)[:, :, L:])
