@@ -38,9 +38,8 @@ def _out(t, name, dtype, shape, device):
     shape = tuple(int(x) for x in shape)
     if t is None:
         return torch.empty(shape, dtype=dtype, device=device)
-    _need(t, name, dtype)
-    if tuple(t.shape) != shape:
-        raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+    _need(t, name, dtype, shape=shape)
+    _on_gpu(t, name)
     return t
 
 
@@ -49,20 +48,41 @@ def _scratch(t, name, nbytes, device):
     if t is None:
         return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
     _need(t, name)
+    _on_gpu(t, name)
     return t
 
 
-def _need(t, name, dtype=None, ndim=None):
+def _need(t, name, dtype=None, ndim=None, shape=None):
+    """Type, dtype, rank, exact shape and contiguity of one tensor argument.
+
+    Every tensor the kernels read or write is checked against the sizes the call
+    derives, so a short or mis-shaped buffer is refused here instead of being read
+    or written past its end on the device.  The device is checked separately
+    (``_on_gpu``), after all shapes, so shape errors read the same on any device.
+    """
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(*named):
+    """named: tensor, name, tensor, name, ... (None tensors are skipped)."""
+    for t, name in zip(named[::2], named[1::2]):
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _blocks32(T, name):
+    if T % 32 != 0:
+        raise ValueError(f"{name} has {T} tokens, not a multiple of the 32-token block")
+    return T // 32
 
 
 def swa_prefill(q, k, v, window: int, scale: float | None = None, out=None, ring_k=None, ring_v=None,
@@ -73,21 +93,27 @@ def swa_prefill(q, k, v, window: int, scale: float | None = None, out=None, ring
     Optional ring_k/ring_v [B, Hkv, W, D] receive the last W tokens' K/V at
     slot position mod W.  Returns out shaped like q.
     """
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a torch.Tensor")
     squeeze = q.dim() == 3
     dtype = q.dtype
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _need(t, name, dtype, 3 if squeeze else 4)
     if dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("dtype must be bfloat16 or float32")
+    _need(q, "q", dtype, 3 if squeeze else 4)
     B, L, Hq, D = (1, *q.shape) if squeeze else q.shape
+    _need(k, "k", dtype, q.dim())
     Hkv = k.shape[-2]
-    out = _out(out, "out", q.dtype, q.shape, q.device)
-    _need(out, "out", dtype)
+    kv_shape = (L, Hkv, D) if squeeze else (B, L, Hkv, D)
+    _need(k, "k", dtype, shape=kv_shape)
+    _need(v, "v", dtype, shape=kv_shape)
     W = 0
     if ring_k is not None or ring_v is not None:
         _need(ring_k, "ring_k", dtype, 4)
-        _need(ring_v, "ring_v", dtype, 4)
         W = ring_k.shape[2]
+        _need(ring_k, "ring_k", dtype, shape=(B, Hkv, W, D))
+        _need(ring_v, "ring_v", dtype, shape=(B, Hkv, W, D))
+    _on_gpu(q, "q", k, "k", v, "v", ring_k, "ring_k", ring_v, "ring_v")
+    out = _out(out, "out", q.dtype, q.shape, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(_lib.load().swa_prefill(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, L, Hq, Hkv, D, int(window), scale,
@@ -103,13 +129,15 @@ def swa_decode_ring(q, k_new, v_new, ring_k, ring_v, pos, scale: float | None = 
     updated in place); pos [B] int32.  Returns (out [B, Hq, D], slot_out [B] int32).
     """
     _need(q, "q", torch.bfloat16, 3)
-    _need(k_new, "k_new", torch.bfloat16, 3)
-    _need(v_new, "v_new", torch.bfloat16, 3)
     _need(ring_k, "ring_k", torch.bfloat16, 4)
-    _need(ring_v, "ring_v", torch.bfloat16, 4)
-    _need(pos, "pos", torch.int32, 1)
     B, Hq, D = q.shape
     Hkv, W = ring_k.shape[1], ring_k.shape[2]
+    _need(ring_k, "ring_k", torch.bfloat16, shape=(B, Hkv, W, D))
+    _need(ring_v, "ring_v", torch.bfloat16, shape=(B, Hkv, W, D))
+    _need(k_new, "k_new", torch.bfloat16, shape=(B, Hkv, D))
+    _need(v_new, "v_new", torch.bfloat16, shape=(B, Hkv, D))
+    _need(pos, "pos", torch.int32, shape=(B,))
+    _on_gpu(q, "q", k_new, "k_new", v_new, "v_new", ring_k, "ring_k", ring_v, "ring_v", pos, "pos")
     out = _out(out, "out", q.dtype, q.shape, q.device)
     slot_out = _out(slot_out, "slot_out", torch.int32, (B,), q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
@@ -126,14 +154,41 @@ def kv_quant_int8_b32(x, codes=None, scales=None, stream=None):
     """
     _need(x, "x", torch.bfloat16, 4)
     B, Hkv, T, D = x.shape
+    nblk = _blocks32(T, "x")
+    _on_gpu(x, "x")
     codes = _out(codes, "codes", torch.int8, x.shape, x.device)
-    scales = _out(scales, "scales", torch.float32, (B, Hkv, T // 32), x.device)
+    scales = _out(scales, "scales", torch.float32, (B, Hkv, nblk), x.device)
     _check(_lib.load().kv_quant_int8_b32(_ptr(x), _ptr(codes), _ptr(scales), B, Hkv, T, D, _stream(stream)))
     return codes, scales
 
 
 def attn_decode_int8kv_workspace_size(B, Hq, Hkv, D, T8, Th) -> int:
     return int(_lib.load().attn_decode_int8kv_workspace_size(B, Hq, Hkv, D, T8, Th))
+
+
+def _int8_pool(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot, k_means=None, with_means=False):
+    """Checks the INT8 + bf16 pool arguments of the decodes; returns (B, Hq, Hkv, D, T8, Th)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_hot, "k_hot", torch.bfloat16, 4)
+    B, Hq, D = q.shape
+    Hkv, Th = k_hot.shape[1], k_hot.shape[2]
+    _need(k_hot, "k_hot", torch.bfloat16, shape=(B, Hkv, Th, D))
+    _need(v_hot, "v_hot", torch.bfloat16, shape=(B, Hkv, Th, D))
+    T8 = 0 if k_codes is None else int(k_codes.shape[2]) if k_codes.dim() == 4 else -1
+    if k_codes is not None:
+        _need(k_codes, "k_codes", torch.int8, 4)
+    if T8 > 0:
+        nblk = _blocks32(T8, "k_codes")
+        _need(k_codes, "k_codes", torch.int8, shape=(B, Hkv, T8, D))
+        _need(v_codes, "v_codes", torch.int8, shape=(B, Hkv, T8, D))
+        _need(k_scales, "k_scales", torch.float32, shape=(B, Hkv, nblk))
+        _need(v_scales, "v_scales", torch.float32, shape=(B, Hkv, nblk))
+        if with_means:
+            _need(k_means, "k_means", torch.float32, shape=(B, Hkv, D, nblk))
+        _on_gpu(k_codes, "k_codes", v_codes, "v_codes", k_scales, "k_scales", v_scales, "v_scales",
+                k_means if with_means else None, "k_means")
+    _on_gpu(q, "q", k_hot, "k_hot", v_hot, "v_hot")
+    return B, Hq, Hkv, D, T8, Th
 
 
 def attn_decode_int8kv(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot, scale: float | None = None,
@@ -143,17 +198,7 @@ def attn_decode_int8kv(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot, sc
     q [B, Hq, D] bf16; *_codes [B, Hkv, T8, D] int8; *_scales [B, Hkv, T8/32] fp32;
     *_hot [B, Hkv, Th, D] bf16.  Returns out [B, Hq, D] bf16.
     """
-    _need(q, "q", torch.bfloat16, 3)
-    _need(k_hot, "k_hot", torch.bfloat16, 4)
-    _need(v_hot, "v_hot", torch.bfloat16, 4)
-    B, Hq, D = q.shape
-    Hkv, Th = k_hot.shape[1], k_hot.shape[2]
-    T8 = 0 if k_codes is None else k_codes.shape[2]
-    if T8 > 0:
-        _need(k_codes, "k_codes", torch.int8, 4)
-        _need(v_codes, "v_codes", torch.int8, 4)
-        _need(k_scales, "k_scales", torch.float32, 3)
-        _need(v_scales, "v_scales", torch.float32, 3)
+    B, Hq, Hkv, D, T8, Th = _int8_pool(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot)
     out = _out(out, "out", torch.bfloat16, q.shape, q.device)
     need = attn_decode_int8kv_workspace_size(B, Hq, Hkv, D, T8, Th)
     workspace = _scratch(workspace, "workspace", need, q.device)
@@ -179,9 +224,13 @@ def blocksparse_select_attend(q, k, v, block: int = 64, topk: int = 64, window: 
     """
     _need(q, "q", torch.bfloat16, 3)
     _need(k, "k", torch.bfloat16, 3)
-    _need(v, "v", torch.bfloat16, 3)
     L, Hq, D = q.shape
     Hkv = k.shape[1]
+    _need(k, "k", torch.bfloat16, shape=(L, Hkv, D))
+    _need(v, "v", torch.bfloat16, shape=(L, Hkv, D))
+    if block <= 0 or L % block != 0:
+        raise ValueError(f"L = {L} must be a multiple of block = {block}")
+    _on_gpu(q, "q", k, "k", v, "v")
     out = _out(out, "out", torch.bfloat16, q.shape, q.device)
     sel = _out(sel, "sel", torch.int32, (Hq, L // block, topk), q.device)
     need = blocksparse_workspace_size(L, Hq, Hkv, D, block, topk)
@@ -200,10 +249,9 @@ def swa_window_safe_len(slot_pos, match_len, out=None, stream=None):
     int32.  Returns safe_len [B] int32.
     """
     _need(slot_pos, "slot_pos", torch.int32, 2)
-    _need(match_len, "match_len", torch.int32, 1)
     B, W = slot_pos.shape
-    if match_len.shape[0] != B:
-        raise ValueError("match_len must have one entry per sequence")
+    _need(match_len, "match_len", torch.int32, shape=(B,))
+    _on_gpu(slot_pos, "slot_pos", match_len, "match_len")
     out = _out(out, "out", torch.int32, (B,), slot_pos.device)
     _check(_lib.load().swa_window_safe_len(_ptr(slot_pos), _ptr(match_len), _ptr(out), B, W, _stream(stream)))
     return out
@@ -217,12 +265,14 @@ def swa_prefill_chunk(q, k, v, ring_k, ring_v, pos0: int, scale: float | None = 
     The window is the ring size W.  Returns out [B, C, Hq, D].
     """
     _need(q, "q", torch.bfloat16, 4)
-    _need(k, "k", torch.bfloat16, 4)
-    _need(v, "v", torch.bfloat16, 4)
     _need(ring_k, "ring_k", torch.bfloat16, 4)
-    _need(ring_v, "ring_v", torch.bfloat16, 4)
     B, C, Hq, D = q.shape
     Hkv, W = ring_k.shape[1], ring_k.shape[2]
+    _need(k, "k", torch.bfloat16, shape=(B, C, Hkv, D))
+    _need(v, "v", torch.bfloat16, shape=(B, C, Hkv, D))
+    _need(ring_k, "ring_k", torch.bfloat16, shape=(B, Hkv, W, D))
+    _need(ring_v, "ring_v", torch.bfloat16, shape=(B, Hkv, W, D))
+    _on_gpu(q, "q", k, "k", v, "v", ring_k, "ring_k", ring_v, "ring_v")
     out = _out(out, "out", q.dtype, q.shape, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(_lib.load().swa_prefill_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ring_k), _ptr(ring_v),
@@ -236,9 +286,11 @@ def kv_block_means_int8(codes, scales, means=None, stream=None):
     Returns means float32 [B, Hkv, D, T8/32] (d-major).
     """
     _need(codes, "codes", torch.int8, 4)
-    _need(scales, "scales", torch.float32, 3)
     B, Hkv, T8, D = codes.shape
-    means = _out(means, "means", torch.float32, (B, Hkv, D, T8 // 32), codes.device)
+    nblk = _blocks32(T8, "codes")
+    _need(scales, "scales", torch.float32, shape=(B, Hkv, nblk))
+    _on_gpu(codes, "codes", scales, "scales")
+    means = _out(means, "means", torch.float32, (B, Hkv, D, nblk), codes.device)
     _check(_lib.load().kv_block_means_int8(_ptr(codes), _ptr(scales), _ptr(means), B, Hkv, T8, D,
                                            _stream(stream)))
     return means
@@ -254,18 +306,8 @@ def attn_decode_int8kv_sparse(q, k_codes, k_scales, v_codes, v_scales, k_means, 
 
     Returns (out [B, Hq, D] bf16, sel [B, Hq, topk] int32).
     """
-    _need(q, "q", torch.bfloat16, 3)
-    _need(k_hot, "k_hot", torch.bfloat16, 4)
-    _need(v_hot, "v_hot", torch.bfloat16, 4)
-    B, Hq, D = q.shape
-    Hkv, Th = k_hot.shape[1], k_hot.shape[2]
-    T8 = 0 if k_codes is None else k_codes.shape[2]
-    if T8:
-        _need(k_codes, "k_codes", torch.int8, 4)
-        _need(v_codes, "v_codes", torch.int8, 4)
-        _need(k_scales, "k_scales", torch.float32, 3)
-        _need(v_scales, "v_scales", torch.float32, 3)
-        _need(k_means, "k_means", torch.float32, 4)
+    B, Hq, Hkv, D, T8, Th = _int8_pool(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot, k_means,
+                                       with_means=True)
     out = _out(out, "out", torch.bfloat16, q.shape, q.device)
     sel = _out(sel, "sel", torch.int32, (B, Hq, topk), q.device)
     need = attn_decode_int8kv_sparse_workspace_size(B, Hq, Hkv, D, T8, Th, topk)

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(D) void int8_combine_kernel(Int8DecodeArgs a) {
   constexpr int CH = 256;  // splits weighed per pass
   __shared__ float sf[CH];
   __shared__ float red[D / 64];
-  __shared__ float s_M, s_L;
+  __shared__ float s_M;
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int G = a.Hq / a.Hkv;
@@ -209,7 +209,6 @@ __global__ __launch_bounds__(D) void int8_combine_kernel(Int8DecodeArgs a) {
     float M = kNegInf;
     for (int i = 0; i < D / 64; ++i) M = fmaxf(M, red[i]);
     s_M = M;
-    s_L = 0.f;
   }
   __syncthreads();
   const float M = s_M;

@@ -7,8 +7,7 @@ import torch
 
 from hybrid_swa_kv_amd import synth
 
-BF16_TOL = 2e-2   # max-abs tolerance for bf16 outputs (see bf16_excess)
-BF16_REL = 2.0 ** -7  # above |ref| = 2.56 the bf16 format itself cannot hold 2e-2
+BF16_TOL = 2e-2   # max-abs tolerance of the arithmetic for bf16 outputs (see bf16_excess)
 F32_TOL = 1e-5    # max-abs tolerance for fp32 outputs
 
 
@@ -36,19 +35,34 @@ def max_abs(a, b) -> float:
     return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)))) if np.size(a) else 0.0
 
 
-def bf16_excess(got, ref) -> float:
-    """Largest |got - ref| - max(2e-2, 2^-7 |ref|) over all elements (<= 0 passes).
+def half_ulp_bf16(x) -> np.ndarray:
+    """Half a bf16 unit in the last place of |x| (the largest rounding error of a
+    bf16 result near x): 2^(e - 9) for |x| = m 2^e, m in [0.5, 1); 2^-134 (half
+    the smallest subnormal step) below the normal range."""
+    a = np.abs(np.asarray(x, np.float64))
+    _, e = np.frexp(a)
+    return np.where(a >= 2.0 ** -126, np.ldexp(1.0, e - 9), 2.0 ** -134)
 
-    A bf16 output is itself rounded by up to half an ulp, 2^-9 |x|, which exceeds
-    2e-2 once |x| >= 8; the absolute bar therefore turns into a relative bar of
-    2^-7 (one to two bf16 ulps) where 2^-7 |ref| > 2e-2, i.e. for |ref| > 2.56.
+
+def bf16_excess(got, ref, label: str = "") -> float:
+    """Largest |got - ref| - (2e-2 + half_ulp_bf16(ref)) over all elements (<= 0 passes).
+
+    2e-2 bounds the error of the arithmetic; a bf16 output also carries its own
+    final rounding, up to half an ulp of the value, which is between 2^-9 |x| and
+    2^-8 |x| and exceeds 2e-2 from |x| >= 8 on (the x8 outliers of the INT8
+    workload produce such outputs).  The number of elements whose error is above
+    2e-2, i.e. that needed the half-ulp term, is printed.
     """
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     if got.size == 0:
         return -1.0
-    allowed = np.maximum(BF16_TOL, BF16_REL * np.abs(ref))
-    return float(np.max(np.abs(got - ref) - allowed))
+    err = np.abs(got - ref)
+    n_extra = int(np.count_nonzero(err > BF16_TOL))
+    if n_extra:
+        print(f"[bf16] {label} {n_extra} of {err.size} elements above 2e-2 (within 2e-2 + half ulp: "
+              f"{int(np.count_nonzero(err <= BF16_TOL + half_ulp_bf16(ref)))})", flush=True)
+    return float(np.max(err - (BF16_TOL + half_ulp_bf16(ref))))
 
 
 def announce(name: str, **kw) -> None:

@@ -9,6 +9,7 @@ import hybrid_swa_kv_amd as hsk
 import oracle
 from hybrid_swa_kv_amd import synth
 from tests.helpers import announce, bf16_excess, f64, gpu_bf16, max_abs, out_f64
+from tests.test_gpu_blocksparse import near_tie_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +34,9 @@ def _gpu_pool(q, kx, vx, T8):
 
 def check_rows(sel_gpu, scores, topk, rows):
     """Kept blocks equal the oracle's, except where a block sits at an fp64 near-tie
-    with the cut (the order of an fp64 dot product is not fixed)."""
+    with the cut (the order of an fp64 dot product is not fixed).  Returns the
+    number of rows that needed that acceptance; it is printed and bounded."""
+    near = 0
     for (b, h) in rows:
         n = scores.shape[-1]
         got = sel_gpu[b, h]
@@ -49,6 +52,10 @@ def check_rows(sel_gpu, scores, topk, rows):
         for j in a ^ c:
             assert abs(sc[j] - cut) <= tol, ("selection differs away from a tie", b, h, j)
         assert np.array_equal(got[:k], np.sort(got[:k]))
+        near += 1
+    print(f"[select] near-tie rows: {near} of {len(rows)}", flush=True)
+    assert near <= near_tie_bound(len(rows)), ("too many near-tie rows", near, len(rows))
+    return near
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,D,T8,Th,topk", [
@@ -86,36 +93,3 @@ def test_sparse_decode_parity(B, Hq, Hkv, D, T8, Th, topk):
                                            sel_np)
     ex = bf16_excess(out_f64(out), ref)
     assert ex <= 0, (ex, max_abs(out_f64(out), ref))
-
-
-def test_sparse_decode_int8_workload_sampled():
-    """Batch 16, context 65536 (63488 INT8 + 2048 bf16), 32/8 heads, top-64 blocks:
-    the selection and the output of sampled (sequence, head) rows."""
-    announce("sparse_decode_workload")
-    B, Hq, Hkv, D, T8, Th, topk = 16, 32, 8, 128, 63488, 2048, 64
-    q = synth.normal_gpu(1300, synth.Q, (B, Hq, D))
-    kx = synth.normal_gpu(1300, synth.K, (B, Hkv, T8 + Th, D), outlier_p=0.01)
-    vx = synth.normal_gpu(1300, synth.V, (B, Hkv, T8 + Th, D), outlier_p=0.01)
-    kc, ks = hsk.kv_quant_int8_b32(kx[:, :, :T8].contiguous())
-    vc, vs = hsk.kv_quant_int8_b32(vx[:, :, :T8].contiguous())
-    km = hsk.kv_block_means_int8(kc, ks)
-    out, sel = hsk.attn_decode_int8kv_sparse(q, kc, ks, vc, vs, km, kx[:, :, T8:].contiguous(),
-                                             vx[:, :, T8:].contiguous(), topk=topk)
-    torch.cuda.synchronize()
-    rows = [(0, 0), (3, 7), (9, 18), (15, 31)]
-    sel_np = sel.cpu().numpy()
-    for (b, h) in rows:
-        g = h // (Hq // Hkv)
-        kcb, ksb = kc[b:b + 1, g:g + 1].cpu().numpy(), ks[b:b + 1, g:g + 1].cpu().numpy()
-        vcb, vsb = vc[b:b + 1, g:g + 1].cpu().numpy(), vs[b:b + 1, g:g + 1].cpu().numpy()
-        means = oracle.int8_block_means(kcb, ksb)
-        assert np.array_equal(km[b:b + 1, g:g + 1].cpu().numpy(), means.transpose(0, 1, 3, 2))
-        qb = q[b:b + 1, h:h + 1].float().cpu().numpy().astype(np.float64)
-        _, scores = oracle.sparse_select(qb, means, topk, return_scores=True)
-        check_rows(sel_np[b:b + 1, h:h + 1], scores, topk, [(0, 0)])
-        kh = kx[b:b + 1, g:g + 1, T8:].float().cpu().numpy().astype(np.float64)
-        vh = vx[b:b + 1, g:g + 1, T8:].float().cpu().numpy().astype(np.float64)
-        ref = oracle.attn_decode_int8kv_sparse(qb, kcb, ksb, vcb, vsb, kh, vh, sel_np[b:b + 1, h:h + 1])
-        got = out[b:b + 1, h:h + 1].float().cpu().numpy().astype(np.float64)
-        ex = bf16_excess(got, ref)
-        assert ex <= 0, (b, h, ex, max_abs(got, ref))
