@@ -15,6 +15,7 @@ One step is one pass over every operation of the path, each at its workload size
   int8sparse  attn_decode_int8kv_sparse on the same pool: the hot tail plus each
             head's top-64 32-token INT8 blocks (scored by q . block mean)
   sparse  blocksparse_select_attend  L 131072, 32/8 heads, 64-token blocks, top-64, window 1024
+  tiny    swa_prefill       fp32, L 512, 2/2 heads, head_dim 64, window 128 (absolute time)
   hybrid70  one decode step of a 70-layer hybrid stack: 60 swa_decode_ring layers
             (window 128) and 10 full-attention layers (attn_decode_int8kv over an
             all-bf16 context), batch 32, context 32768, one HIP graph; also the
@@ -26,7 +27,10 @@ timed with HIP events on the stream they run on); every other operation is
 reported under "rows" with its own roofline.
 Inputs are seeded synthetic tensors (N(0,1), 1% x8 outliers for the INT8 cache)
 drawn on the GPU and resident in HBM before timing starts.  The CPU oracle is
-timed on a bounded sample of the ring-decode workload ("cpu_baseline").
+timed beside every row on one host core ("cpu_baseline" of each row; the
+top-level one is the ring row's): in full where a sample of whole calls fits a
+few seconds, otherwise on sampled rows, heads or units and extrapolated by
+visible-pair, head, chunk or unit count (marked "extrapolated").
 """
 
 from __future__ import annotations
@@ -46,6 +50,7 @@ PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12   # dense bf16 MFMA, 2516.6 TFLOP/s
 PEAK_HBM_GBS = 8000.0                           # HBM3E, 8 TB/s
 
 # workload shapes
+TINY = dict(L=512, Hq=2, Hkv=2, D=64, W=128)   # the fp32 correctness-sized window prefill
 RING = dict(B=32, Hq=32, Hkv=8, D=128, W=128, ctx=32768, layers=60)
 PREFILL = dict(L=131072, Hq=64, Hkv=8, D=128, W=1024)
 INT8 = dict(B=16, Hq=32, Hkv=8, D=128, ctx=65536, hot=2048)
@@ -267,10 +272,30 @@ class Timer:
                 "calls": len(v)}
 
 
-def cpu_baseline(target_s: float):
-    """The oracle on a bounded sample of the ring-decode workload (one thread)."""
-    import numpy as np
+def _oracle_pool():
+    """Limits BLAS to one thread: every oracle baseline uses exactly one core."""
     from threadpoolctl import threadpool_limits
+    return threadpool_limits(limits=1)
+
+
+def _timed(fn, budget_s, min_calls=1):
+    """Calls fn() until budget_s has passed (at least min_calls); returns (calls, seconds)."""
+    n = 0
+    t0 = time.perf_counter()
+    while n < min_calls or time.perf_counter() - t0 < budget_s:
+        fn()
+        n += 1
+    return n, time.perf_counter() - t0
+
+
+def _baseline(value, unit, sample, extrapolated, seconds):
+    return {"value": value, "unit": unit, "cores": 1, "kind": "oracle", "sample": sample,
+            "extrapolated": extrapolated, "oracle_seconds": round(seconds, 2)}
+
+
+def cpu_ring(budget_s):
+    """The oracle on whole ring-decode steps (every ring layer's append + window attention)."""
+    import numpy as np
 
     import oracle
     from hybrid_swa_kv_amd import synth
@@ -284,26 +309,261 @@ def cpu_baseline(target_s: float):
     start = pos - W
     ring_k = oracle.ring_fill(kseq, start, pos - 1, W, np.zeros((B, Hkv, W, D)))
     ring_v = oracle.ring_fill(vseq, start, pos - 1, W, np.zeros((B, Hkv, W, D)))
-    layers = 0
+
+    def one_step():
+        for _ in range(c["layers"]):
+            oracle.ring_append(ring_k, pos, kseq[:, :, W])
+            oracle.ring_append(ring_v, pos, vseq[:, :, W])
+            oracle.swa_decode(q, kseq, vseq, start, pos, W)
+
+    with _oracle_pool():
+        steps, el = _timed(one_step, budget_s)
+    calls = steps * c["layers"]
+    b = _baseline(round(calls * ring_bytes_per_call() / el / 1e9, 4), "GB/s",
+                  f"{steps} full steps = {calls} ring-decode calls (append + window attention, batch {B}, "
+                  f"{Hq}/{Hkv} heads, window {W}), numpy fp64, one BLAS thread", False, el)
+    b["us_per_call"] = round(el / calls * 1e6, 1)
+    return b
+
+
+def cpu_tiny(budget_s):
+    """The whole tiny fp32 window prefill (L 512, 2/2 heads, head_dim 64, window 128)."""
+    import oracle
+    from hybrid_swa_kv_amd import synth
+
+    c = TINY
+    q = synth.token_major(1, synth.Q, c["L"], c["Hq"], c["D"], dtype="f32")
+    k = synth.token_major(1, synth.K, c["L"], c["Hkv"], c["D"], dtype="f32")
+    v = synth.token_major(1, synth.V, c["L"], c["Hkv"], c["D"], dtype="f32")
+    with _oracle_pool():
+        n, el = _timed(lambda: oracle.swa_prefill(q, k, v, c["W"]), budget_s, 3)
+    return _baseline(round(el / n * 1e6, 1), "us", f"{n} whole calls, numpy fp64", False, el)
+
+
+def cpu_prefill(name, budget_s):
+    """C3 rows: query rows of one head timed, extrapolated to every row and head by
+    visible (query, key) pairs.  A window row's work does not depend on L, so the
+    window rows come from a shorter sequence; full-causal rows span the whole
+    131072-token sequence."""
+    import numpy as np
+
+    import oracle
+    from hybrid_swa_kv_amd import synth
+
+    c = PREFILL
+    W = c["W"] if name == "swa" else 0
+    L = 4096 if W else c["L"]
+    q = synth.token_major(31, synth.Q, L, 1, c["D"], dtype="f32")
+    k = synth.token_major(31, synth.K, L, 1, c["D"], dtype="f32")
+    v = synth.token_major(31, synth.V, L, 1, c["D"], dtype="f32")
+    rng = np.random.default_rng(5)
+    done_rows, pairs = 0, 0
     t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        # whole steps (every ring-decode layer once) until the time budget is used
-        while layers == 0 or time.perf_counter() - t0 < target_s:
-            for _ in range(c["layers"]):
-                oracle.ring_append(ring_k, pos, kseq[:, :, W])
-                oracle.ring_append(ring_v, pos, vseq[:, :, W])
-                oracle.swa_decode(q, kseq, vseq, start, pos, W)
-                layers += 1
+    with _oracle_pool():
+        while done_rows == 0 or time.perf_counter() - t0 < budget_s:
+            rows = np.sort(rng.integers(W, L, size=8)) if W else np.sort(rng.integers(0, L, size=8))
+            oracle.swa_prefill(q, k, v, W, rows=rows, row_block=1 if W else 8)
+            done_rows += len(rows)
+            pairs += int(len(rows) * W) if W else int((rows + 1).sum())
     el = time.perf_counter() - t0
-    return {
-        "value": round(layers * ring_bytes_per_call() / el / 1e9, 4),
-        "unit": "GB/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": f"{layers // c['layers']} full steps = {layers} ring-decode layer calls (append + window "
-                  f"attention, batch {B}, {Hq}/{Hkv} heads, window {W}), numpy fp64, one BLAS thread, {el:.1f} s",
-        "host_cpus": os.cpu_count(),
-    }
+    total_pairs = c["Hq"] * pairs_prefill(c["L"], W)
+    total_s = el * total_pairs / pairs
+    flops = 4 * c["D"] * c["Hq"] * pairs_prefill(c["L"], W)
+    return _baseline(round(flops / total_s / 1e12, 6), "TFLOP/s",
+                     f"{done_rows} query rows of one head ({pairs} visible pairs, numpy fp64), extrapolated by "
+                     f"visible-pair count to all {c['L']} rows x {c['Hq']} heads ({total_s:.0f} s)", True, el)
+
+
+def cpu_chunk(C, budget_s):
+    """One chunk of the window prefill (one query head) timed, extrapolated to every
+    head and chunk by head and chunk count."""
+    import numpy as np
+
+    import oracle
+    from hybrid_swa_kv_amd import synth
+
+    c = PREFILL
+    W, D = c["W"], c["D"]
+    q = synth.normal(32, synth.Q, (1, C, 1, D), 1, "f32")
+    k = synth.normal(32, synth.K, (1, C, 1, D), 1, "f32")
+    v = synth.normal(32, synth.V, (1, C, 1, D), 1, "f32")
+    rk = synth.normal(32, synth.K_NEW, (1, 1, W, D), 1, "f32")
+    rv = synth.normal(32, synth.V_NEW, (1, 1, W, D), 1, "f32")
+    with _oracle_pool():
+        n, el = _timed(lambda: oracle.swa_prefill_chunk(q, k, v, rk, rv, C, W), budget_s)
+    per = el / n
+    chunks = c["L"] // C
+    total_s = per * c["Hq"] * chunks
+    flops = 4 * D * c["Hq"] * pairs_prefill(c["L"], W)
+    return _baseline(round(flops / total_s / 1e12, 6), "TFLOP/s",
+                     f"{n} calls of one {C}-token chunk at position {C} (one head, numpy fp64), extrapolated by "
+                     f"head and chunk count to {c['Hq']} heads x {chunks} chunks ({total_s:.0f} s)", True, el)
+
+
+def _int8_unit(seed, T, hot, D, G):
+    """One (sequence, KV head) unit of the INT8 workload: bf16 K/V values (fp32), q."""
+    from hybrid_swa_kv_amd import synth
+
+    kx = synth.bf16_bits_to_f32(synth.head_major(seed, synth.K, 1, 1, T, D, outlier_p=0.01))
+    vx = synth.bf16_bits_to_f32(synth.head_major(seed, synth.V, 1, 1, T, D, outlier_p=0.01))
+    q = synth.bf16_bits_to_f32(synth.normal(seed, synth.Q, (1, G, D), 1)).astype("float64")
+    return kx, vx, q
+
+
+def cpu_int8(name, budget_s):
+    """INT8 rows, by (sequence, KV head) unit: the encoder on a unit's K and V, the
+    dense decode or the block-sparse decode of its four query heads; extrapolated
+    to the 128 units by unit count."""
+    import numpy as np
+
+    import oracle
+
+    c = INT8
+    T, hot, D = c["ctx"], c["hot"], c["D"]
+    T8, G = T - hot, c["Hq"] // c["Hkv"]
+    units = c["B"] * c["Hkv"]
+    kx, vx, q = _int8_unit(41, T, hot, D, G)
+    kc, ks = oracle.kv_quant_int8_b32(kx[:, :, :T8])
+    vc, vs = oracle.kv_quant_int8_b32(vx[:, :, :T8])
+    kh, vh = kx[:, :, T8:], vx[:, :, T8:]
+    unit_bytes = None
+    if name == "quant":
+        fn = lambda: (oracle.kv_quant_int8_b32(kx[:, :, :T8]), oracle.kv_quant_int8_b32(vx[:, :, :T8]))
+        total_bytes = int8_quant_bytes()
+        what = "K and V of one unit encoded"
+    elif name == "int8":
+        fn = lambda: oracle.attn_decode_int8kv(q, kc, ks, vc, vs, kh, vh)
+        total_bytes = int8_decode_bytes()
+        what = "one unit's dense decode (4 heads)"
+    else:
+        def fn():
+            means = oracle.int8_block_means(kc, ks)
+            sel = oracle.sparse_select(q, means, 64)
+            oracle.attn_decode_int8kv_sparse(q, kc, ks, vc, vs, kh, vh, sel)
+        means = oracle.int8_block_means(kc, ks)
+        sel = oracle.sparse_select(q, means, 64)
+        kept = len(np.unique(sel[sel >= 0]))
+        unit_bytes = (kept * 2 * (32 * D + 4) + 2 * hot * D * 2 + D * (T8 // 32) * 4 + 2 * G * D * 2)
+        total_bytes = unit_bytes * units
+        what = "one unit's block means, top-64 selection and sparse decode (4 heads)"
+    with _oracle_pool():
+        n, el = _timed(fn, budget_s)
+    total_s = el / n * units
+    return _baseline(round(total_bytes / total_s / 1e9, 4), "GB/s",
+                     f"{n} x {what} (numpy; fp32 encoder, fp64 attention), extrapolated by unit count to "
+                     f"{units} units ({total_s:.1f} s)", True, el)
+
+
+def cpu_sparse(budget_s, pairs_total):
+    """Block-sparse prefill: one query head's selection (block sums, scores, top-64)
+    and whole 64-row output tiles timed; extrapolated to 32 heads and every tile."""
+    import numpy as np
+
+    import oracle
+    from hybrid_swa_kv_amd import synth
+
+    c = SPARSE
+    L, D, blk = c["L"], c["D"], c["block"]
+    nb = L // blk
+    q = synth.token_major(51, synth.Q, L, 1, D, dtype="f32")
+    k = synth.token_major(51, synth.K, L, 1, D, dtype="f32")
+    v = synth.token_major(51, synth.V, L, 1, D, dtype="f32")
+    t0 = time.perf_counter()
+    with _oracle_pool():
+        sel = oracle.block_select(q, k, blk, c["topk"])
+        t_sel = time.perf_counter() - t0
+        rng = np.random.default_rng(9)
+        tiles, t1 = 0, time.perf_counter()
+        while tiles == 0 or time.perf_counter() - t0 < budget_s:
+            qb = int(rng.integers(0, nb))
+            oracle.blocksparse_attend(q, k, v, sel, blk, c["W"], rows=np.arange(qb * blk, (qb + 1) * blk))
+            tiles += 1
+        t_tile = (time.perf_counter() - t1) / tiles
+    el = time.perf_counter() - t0
+    total_s = c["Hq"] * (t_sel + nb * t_tile)
+    flops = 4 * D * pairs_total
+    return _baseline(round(flops / total_s / 1e12, 6), "TFLOP/s of visible pairs",
+                     f"one head's selection ({t_sel:.1f} s) and {tiles} random 64-row output tiles (numpy fp64), "
+                     f"extrapolated to {c['Hq']} heads x {nb} tiles ({total_s:.0f} s)", True, el)
+
+
+def cpu_hybrid(budget_s, ring_us_per_call):
+    """70-layer step: the ring layers priced at the ring baseline's time per call, a
+    full layer by (sequence, KV head) unit of its decode over 32768 bf16 tokens."""
+    import numpy as np
+
+    import oracle
+    from hybrid_swa_kv_amd import synth
+
+    c = HYBRID
+    D, G, ctx = c["D"], c["Hq"] // c["Hkv"], c["ctx"]
+    kx = synth.bf16_bits_to_f32(synth.head_major(61, synth.K, 1, 1, ctx, D)).astype(np.float64)
+    vx = synth.bf16_bits_to_f32(synth.head_major(61, synth.V, 1, 1, ctx, D)).astype(np.float64)
+    q = synth.bf16_bits_to_f32(synth.normal(61, synth.Q, (1, G, D), 1)).astype(np.float64)
+    with _oracle_pool():
+        n, el = _timed(lambda: oracle.swa_decode(q, kx, vx, [0], [ctx - 1], 0), budget_s)
+    nfull = sum(hybrid_layers())
+    nswa = c["layers"] - nfull
+    full_layer_s = el / n * c["B"] * c["Hkv"]
+    step_s = nfull * full_layer_s + nswa * ring_us_per_call * 1e-6
+    step_bytes = nswa * ring_bytes_per_call() + nfull * full_decode_bytes()
+    return _baseline(round(step_bytes / step_s / 1e9, 4), "GB/s",
+                     f"{n} x one unit of a full layer's decode (4 heads, {ctx} tokens, numpy fp64), extrapolated "
+                     f"to {c['B'] * c['Hkv']} units x {nfull} full layers, plus {nswa} ring layers at the ring "
+                     f"baseline's time per call ({step_s:.1f} s per step)", True, el)
+
+
+def host_info():
+    """CPU model, logical CPUs and numpy's BLAS thread pools of the host."""
+    model = None
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")} for i in threadpool_info()]
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "blas_pools": blas,
+            "oracle_threads": 1}
+
+
+def source_info():
+    """git commit when the tree is a checkout, and a hash of the library sources."""
+    import hashlib
+    import subprocess
+
+    sha = None
+    try:
+        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
+                             timeout=5).stdout.strip() or None
+    except Exception:
+        pass
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "hybrid_swa_kv_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return {"git_sha": sha, "csrc_sha256": h.hexdigest()[:16]}
+
+
+# seeds of the GPU inputs (synth.normal_gpu(workload, tensor_id, ...), torch Philox)
+SEEDS = {
+    "ring": "workload 2: ring K/V tensor ids 100 + 2l / 101 + 2l, q 1000 + l, k_new 2000 + l, v_new 3000 + l "
+            "for ring set l",
+    "tiny": "synth.token_major(1, Q/K/V) fp32 (PCG64 per head)",
+    "prefill": "workload 3: q, k, v tensor ids 0, 1, 2",
+    "int8": "workload 4: K, V tensor ids 1, 2 (1 % x8 outliers), q 0",
+    "sparse": "workload 5: q, k, v tensor ids 0, 1, 2",
+    "hybrid70": "workload 6: q 100 + i, full-layer K/V 1000 + 2i / 1001 + 2i, rings 3000 + 2i / 3001 + 2i, "
+                "new K/V 5000 + 2i / 5001 + 2i for layer i",
+    "cpu_baseline": "oracle inputs from synth (PCG64) workloads 2, 1, 31, 32, 41, 51, 61",
+}
 
 
 def main() -> int:
@@ -311,8 +571,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--rows", default="ring,int8,int8sparse,quant,swa,full,chunk4096,chunk8192,sparse,hybrid70")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--rows", default="ring,int8,int8sparse,quant,swa,full,chunk4096,chunk8192,sparse,hybrid70,tiny")
+    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+                    help="oracle time for the headline (ring) baseline; every other row gets a third of it")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device-to-device copy (the reference kernel for "
@@ -482,6 +743,13 @@ def main() -> int:
         hybrid_graph = capture(hlayers)
         full_graph = capture([ly for ly in hlayers if ly[0] == "full"])   # the 10 full layers alone
         work["hybrid70"] = hybrid_graph.replay
+    if "tiny" in rows:
+        c = TINY
+        tq = synth.to_torch(synth.token_major(1, synth.Q, c["L"], c["Hq"], c["D"], dtype="f32"), dev)
+        tk = synth.to_torch(synth.token_major(1, synth.K, c["L"], c["Hkv"], c["D"], dtype="f32"), dev)
+        tv = synth.to_torch(synth.token_major(1, synth.V, c["L"], c["Hkv"], c["D"], dtype="f32"), dev)
+        tout = torch.empty_like(tq)
+        work["tiny"] = lambda: hsk.swa_prefill(tq, tk, tv, TINY["W"], out=tout)
     if args.calib_copy:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -588,6 +856,13 @@ def main() -> int:
                          "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                          "kv_tile_bytes": tb, "kv_tile_GB/s": round(tb / (ms * 1e-3) / 1e9, 1)}
 
+    if "tiny" in rows:
+        c = TINY
+        ms = timer.mean_ms("tiny", args.warmup)
+        flops = 4 * c["D"] * c["Hq"] * pairs_prefill(c["L"], c["W"])
+        res["tiny"] = {"us": round(ms * 1e3, 2), "flop": flops, "dtype": "f32",
+                       "note": "correctness-sized fp32 window prefill (L 512, 2/2 heads, head_dim 64, "
+                               "window 128): absolute time only"}
     if "hybrid70" in rows:
         c = HYBRID
         ms = timer.mean_ms("hybrid70", args.warmup)
@@ -648,9 +923,38 @@ def main() -> int:
                       "compute_units": props.multi_processor_count,
                       "peaks_used": {"bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS,
                                      "basis": "256 CUs x 2.4 GHz x 4096 bf16 FLOP/clk; 8 TB/s HBM3E"}}
+    line["host"] = host_info()
+    line["source"] = source_info()
+    line["seeds"] = SEEDS
     if not args.no_cpu:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        # the oracle beside every row, on the host, one thread (rank 0, one GPU)
+        per = args.cpu_seconds / 3
+        for name in rows:
+            if name not in res or not isinstance(res[name], dict):
+                continue
+            print(f"[bench] cpu baseline (oracle): {name}", file=sys.stderr, flush=True)
+            if name == "ring":
+                b = cpu_ring(args.cpu_seconds)
+            elif name == "tiny":
+                b = cpu_tiny(per)
+            elif name in ("swa", "full"):
+                b = cpu_prefill(name, per)
+            elif name.startswith("chunk"):
+                b = cpu_chunk(int(name[5:]), per)
+            elif name in ("quant", "int8", "int8sparse"):
+                b = cpu_int8(name, per)
+            elif name == "sparse":
+                b = cpu_sparse(per, res["sparse"]["visible_pairs"])
+            elif name == "hybrid70":
+                ring_us = res.get("ring", {}).get("cpu_baseline", {}).get("us_per_call")
+                if ring_us is None:
+                    ring_us = cpu_ring(per)["us_per_call"]
+                b = cpu_hybrid(per, ring_us)
+            else:
+                continue
+            res[name]["cpu_baseline"] = b
+        if "ring" in res:
+            line["cpu_baseline"] = res["ring"]["cpu_baseline"]
     print(json.dumps(line), flush=True)
     return 0
 
