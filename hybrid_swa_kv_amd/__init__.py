@@ -9,6 +9,7 @@ raises if it is missing.
 from .api import (  # noqa: F401
     attn_decode_int8kv,
     attn_decode_int8kv_workspace_size,
+    attn_decode_int8kv_noalloc,
     attn_decode_int8kv_sparse,
     attn_decode_int8kv_sparse_workspace_size,
     kv_block_means_int8,

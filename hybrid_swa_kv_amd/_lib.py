@@ -6,7 +6,7 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhybrid_swa_kv.so")
-ABI_VERSION = 4  # the signatures below; hsk_abi_version() of the loaded library must match
+ABI_VERSION = 5  # the signatures below; hsk_abi_version() of the loaded library must match
 
 # every symbol declared in include/hybrid_swa_kv.h
 EXPORTS = (
@@ -17,6 +17,7 @@ EXPORTS = (
     "kv_quant_int8_b32",
     "attn_decode_int8kv",
     "attn_decode_int8kv_workspace_size",
+    "attn_decode_int8kv_noalloc",
     "blocksparse_select_attend",
     "blocksparse_workspace_size",
     "swa_window_safe_len",
@@ -36,6 +37,7 @@ _SIGS = {
     "kv_quant_int8_b32": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "attn_decode_int8kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
     "attn_decode_int8kv_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
+    "attn_decode_int8kv_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "blocksparse_select_attend": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
     "blocksparse_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "swa_window_safe_len": (_I, [_P, _P, _P, _I, _I, _P]),

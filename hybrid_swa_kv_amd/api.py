@@ -211,6 +211,21 @@ def attn_decode_int8kv(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot, sc
     return out
 
 
+def attn_decode_int8kv_noalloc(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot, scale: float | None = None,
+                               out=None, stream=None):
+    """attn_decode_int8kv with the split records in the library's static device
+    array (no workspace argument; nothing allocated when ``out`` is given).
+    Calls that overlap on one GPU race on that array."""
+    B, Hq, Hkv, D, T8, Th = _int8_pool(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot)
+    out = _out(out, "out", torch.bfloat16, q.shape, q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(_lib.load().attn_decode_int8kv_noalloc(
+        _ptr(q), _ptr(k_codes) if T8 else None, _ptr(k_scales) if T8 else None,
+        _ptr(v_codes) if T8 else None, _ptr(v_scales) if T8 else None, _ptr(k_hot), _ptr(v_hot),
+        _ptr(out), B, Hq, Hkv, D, T8, Th, scale, _stream(stream)))
+    return out
+
+
 def blocksparse_workspace_size(L, Hq, Hkv, D, block=64, topk=64) -> int:
     return int(_lib.load().blocksparse_workspace_size(L, Hq, Hkv, D, block, topk))
 

@@ -11,7 +11,8 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;  // 2: swa_window_safe_len, 3: swa_prefill_chunk, 4: sparse INT8 decode
+constexpr int kAbiVersion = 5;  // 2: swa_window_safe_len, 3: swa_prefill_chunk, 4: sparse INT8 decode,
+                                 // 5: attn_decode_int8kv_noalloc
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -70,6 +71,27 @@ SparsePlan sparse_plan(int B, int Hq, int Hkv, int D, int T8, int Th, int topk) 
 }
 
 }  // namespace
+
+namespace hsk {
+
+int int8_decode_validate(const void* q, const int8_t* k_codes, const float* k_scales, const int8_t* v_codes,
+                         const float* v_scales, const void* k_hot, const void* v_hot, const void* out, int B,
+                         int Hq, int Hkv, int D, int T8, int Th, float scale) {
+  if (!q || !k_hot || !v_hot || !out) return HSK_ERR_NULL;
+  if (T8 > 0 && (!k_codes || !k_scales || !v_codes || !v_scales)) return HSK_ERR_NULL;
+  if (B <= 0 || T8 < 0 || T8 % 32 != 0 || Th <= 0) return HSK_ERR_SHAPE;
+  if (int rc = check_heads(Hq, Hkv, D)) return rc;
+  if (Hq / Hkv > 16) return HSK_ERR_UNSUPPORTED;
+  if ((long long)T8 * D >= (1ll << 31)) return HSK_ERR_UNSUPPORTED;  // 32-bit code offsets per head
+  if ((long long)T8 + 2ll * Th >= (1ll << 31)) return HSK_ERR_UNSUPPORTED;  // 32-bit split weights
+  if (!std::isfinite(scale)) return HSK_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_hot) || !aligned16(v_hot) || !aligned16(out)) return HSK_ERR_ALIGN;
+  if (T8 > 0 && (!aligned16(k_codes) || !aligned16(v_codes) || !aligned4(k_scales) || !aligned4(v_scales)))
+    return HSK_ERR_ALIGN;
+  return HSK_OK;
+}
+
+}  // namespace hsk
 
 extern "C" {
 
@@ -211,17 +233,9 @@ int attn_decode_int8kv(const void* q, const int8_t* k_codes, const float* k_scal
                        const float* v_scales, const void* k_hot, const void* v_hot, void* out, int B, int Hq,
                        int Hkv, int D, int T8, int Th, float scale, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  if (!q || !k_hot || !v_hot || !out) return HSK_ERR_NULL;
-  if (T8 > 0 && (!k_codes || !k_scales || !v_codes || !v_scales)) return HSK_ERR_NULL;
-  if (B <= 0 || T8 < 0 || T8 % 32 != 0 || Th <= 0) return HSK_ERR_SHAPE;
-  if (int rc = check_heads(Hq, Hkv, D)) return rc;
-  if (Hq / Hkv > 16) return HSK_ERR_UNSUPPORTED;
-  if ((long long)T8 * D >= (1ll << 31)) return HSK_ERR_UNSUPPORTED;  // 32-bit code offsets per head
-  if ((long long)T8 + 2ll * Th >= (1ll << 31)) return HSK_ERR_UNSUPPORTED;  // 32-bit split weights
-  if (!std::isfinite(scale)) return HSK_ERR_SHAPE;
-  if (!aligned16(q) || !aligned16(k_hot) || !aligned16(v_hot) || !aligned16(out)) return HSK_ERR_ALIGN;
-  if (T8 > 0 && (!aligned16(k_codes) || !aligned16(v_codes) || !aligned4(k_scales) || !aligned4(v_scales)))
-    return HSK_ERR_ALIGN;
+  if (int rc = hsk::int8_decode_validate(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot, out, B, Hq, Hkv,
+                                         D, T8, Th, scale))
+    return rc;
   const size_t need = int8_ws_bytes(B, Hq, Hkv, D, T8, Th);
   if (!workspace || workspace_bytes < need) return HSK_ERR_WORKSPACE;
   if (!aligned16(workspace)) return HSK_ERR_ALIGN;

@@ -127,6 +127,12 @@ struct SparseDecodeArgs {
   float scale_log2;
 };
 
+// Host-side argument checks of attn_decode_int8kv, everything but the workspace
+// (an HSK_* status; no HIP call).
+int int8_decode_validate(const void* q, const int8_t* k_codes, const float* k_scales, const int8_t* v_codes,
+                         const float* v_scales, const void* k_hot, const void* v_hot, const void* out, int B,
+                         int Hq, int Hkv, int D, int T8, int Th, float scale);
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_ring(const RingCopyArgs& a, hipStream_t s);

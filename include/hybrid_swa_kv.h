@@ -12,7 +12,8 @@
  * ---------------------------------------
  * - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
  *   never allocates, frees or keeps device memory between calls, holds no global
- *   state, and is reentrant.  Work is enqueued on `stream` (a hipStream_t passed
+ *   state, and is reentrant -- except attn_decode_int8kv_noalloc, which uses a
+ *   static device array of its own (see there).  Work is enqueued on `stream` (a hipStream_t passed
  *   as void*; NULL = the null stream) and the call returns without waiting.
  * - Tensors are dense, row-major, contiguous; base pointers must be 16-byte
  *   aligned.  bf16 means IEEE bfloat16 bit patterns (uint16).
@@ -172,6 +173,34 @@ int attn_decode_int8kv(const void* q,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 size_t attn_decode_int8kv_workspace_size(int B, int Hq, int Hkv, int D, int T8, int Th);
+
+/*
+ * attn_decode_int8kv_noalloc — attn_decode_int8kv with no workspace argument.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, semantics, kernels and results as attn_decode_int8kv, bit for bit;
+ * the split records go to a static device array of
+ * ATTN_DECODE_INT8KV_NOALLOC_MAX_WORKSPACE bytes inside the library (one per
+ * GPU, held until the process ends) instead of a caller workspace.
+ * Nothing is allocated and nothing must be cleared between calls.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams or from different host threads) race and must not be
+ * issued; calls ordered on one stream are fine.
+ * Errors: as attn_decode_int8kv; HSK_ERR_WORKSPACE when
+ * attn_decode_int8kv_workspace_size(...) exceeds the array (B * Hkv units of
+ * Hq / Hkv heads and about 2048 / (B * Hkv) splits, (D + 2) floats per split and
+ * head: e.g. 4.3 MB for B 16, 32/8 heads, D 128), checked before any HIP call;
+ * HSK_ERR_HIP when the array's device address cannot be obtained.
+ */
+#define ATTN_DECODE_INT8KV_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)
+
+int attn_decode_int8kv_noalloc(const void* q,
+                               const int8_t* k_codes, const float* k_scales,
+                               const int8_t* v_codes, const float* v_scales,
+                               const void* k_hot, const void* v_hot, void* out,
+                               int B, int Hq, int Hkv, int D, int T8, int Th, float scale,
+                               void* stream);
 
 /*
  * kv_block_means_int8 — the K block means stored with the INT8 blocks.

@@ -99,6 +99,20 @@ def test_int8_decode_validation(lib):
     assert f(P, P, P, P, P, MIS, P, P, 16, 32, 8, 128, 63488, 2048, 1.0, P, need, None) == ALIGN
 
 
+def test_int8_decode_noalloc_validation(lib):
+    """Errors of the static-array variant come back before any HIP call (no GPU
+    needed): argument errors as the workspace entry point's, sizes beyond its
+    32 MiB array as a workspace error."""
+    f = lib.attn_decode_int8kv_noalloc
+    #        q kc ks vc vs kh vh out B Hq Hkv D T8 Th scale stream
+    assert f(P, None, P, P, P, P, P, P, 16, 32, 8, 128, 64, 8, 1.0, None) == NULL
+    assert f(P, P, P, P, P, P, P, P, 16, 32, 8, 128, 48, 8, 1.0, None) == SHAPE
+    assert f(P, P, P, P, P, P, P, P, 16, 32, 8, 128, 64, 0, 1.0, None) == SHAPE
+    assert f(P, P, P, P, P, P, P, P, 1, 34, 2, 128, 64, 8, 1.0, None) == UNSUP
+    assert lib.attn_decode_int8kv_workspace_size(512, 128, 8, 128, 0, 64) > 32 << 20
+    assert f(P, None, None, None, None, P, P, P, 512, 128, 8, 128, 0, 64, 1.0, None) == WS
+
+
 def test_blocksparse_validation(lib):
     f = lib.blocksparse_select_attend
     need = lib.blocksparse_workspace_size(131072, 32, 8, 128, 64, 64)
