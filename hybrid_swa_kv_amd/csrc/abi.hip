@@ -187,6 +187,7 @@ int swa_decode_ring(const void* q, const void* k_new, const void* v_new, void* r
                     int W, float scale, void* stream) {
   if (!q || !k_new || !v_new || !ring_k || !ring_v || !pos || !out) return HSK_ERR_NULL;
   if (B <= 0 || W <= 0 || W > 65536) return HSK_ERR_SHAPE;
+  if (B > 65535) return HSK_ERR_UNSUPPORTED;  // the sequence index is the grid's y dimension
   if (int rc = check_heads(Hq, Hkv, D)) return rc;
   if (Hq / Hkv > 16 && (Hq / Hkv) % 16 != 0) return HSK_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return HSK_ERR_SHAPE;
@@ -203,6 +204,7 @@ int swa_decode_ring(const void* q, const void* k_new, const void* v_new, void* r
   a.out = (uint16_t*)out;
   a.slot_out = slot_out;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.W = W;
+  a.G = Hq / Hkv;
   a.scale_log2 = log2e_times(scale);
   return finish(hsk::launch_ring_decode(a, (hipStream_t)stream));
 }

@@ -35,17 +35,20 @@ struct RingShared {
   uint16_t in[(16 + 2) * D];
 };
 
-template <int D>
+// Grid (Hkv * nhg, B): blockIdx.y is the sequence, blockIdx.x the KV head and
+// head group; with at most 16 heads per KV head (ONE_HG, nhg = 1) nothing is
+// divided before the ring loads are issued (G comes from the host).
+template <int D, bool ONE_HG>
 __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs a) {
   __shared__ __attribute__((aligned(16))) RingShared<D> sh;
   uint16_t* const sm_in = sh.in;
 
-  const int G = a.Hq / a.Hkv;
-  const int HG = G < 16 ? G : 16;  // heads served by this workgroup
-  const int nhg = G / HG;
-  const int hg = blockIdx.x % nhg;
-  const int g = (blockIdx.x / nhg) % a.Hkv;
-  const int b = blockIdx.x / (nhg * a.Hkv);
+  const int G = a.G;
+  const int HG = ONE_HG ? G : 16;  // heads served by this workgroup
+  const int nhg = ONE_HG ? 1 : G / 16;
+  const int hg = ONE_HG ? 0 : (int)blockIdx.x % nhg;
+  const int g = ONE_HG ? (int)blockIdx.x : (int)blockIdx.x / nhg;
+  const int b = blockIdx.y;
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int W = a.W;
@@ -135,13 +138,15 @@ __global__ __launch_bounds__(RD_THREADS) void ring_decode_kernel(RingDecodeArgs 
 }  // namespace
 
 hipError_t launch_ring_decode(const RingDecodeArgs& a, hipStream_t s) {
-  const int G = a.Hq / a.Hkv;
-  const int nhg = G <= 16 ? 1 : G / 16;
-  const int grid = a.B * a.Hkv * nhg;
-  if (a.D == 128)
-    hipLaunchKernelGGL(ring_decode_kernel<128>, dim3(grid), dim3(RD_THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL(ring_decode_kernel<64>, dim3(grid), dim3(RD_THREADS), 0, s, a);
+  const int nhg = a.G <= 16 ? 1 : a.G / 16;
+  const dim3 grid(a.Hkv * nhg, a.B);
+  if (a.D == 128) {
+    if (nhg == 1) hipLaunchKernelGGL((ring_decode_kernel<128, true>), grid, dim3(RD_THREADS), 0, s, a);
+    else hipLaunchKernelGGL((ring_decode_kernel<128, false>), grid, dim3(RD_THREADS), 0, s, a);
+  } else {
+    if (nhg == 1) hipLaunchKernelGGL((ring_decode_kernel<64, true>), grid, dim3(RD_THREADS), 0, s, a);
+    else hipLaunchKernelGGL((ring_decode_kernel<64, false>), grid, dim3(RD_THREADS), 0, s, a);
+  }
   return hipGetLastError();
 }
 

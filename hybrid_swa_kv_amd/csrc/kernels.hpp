@@ -45,6 +45,7 @@ struct RingDecodeArgs {
   uint16_t* out;          // [B, Hq, D]
   int32_t* slot_out;      // [B] or null
   int B, Hq, Hkv, D, W;
+  int G;                  // Hq / Hkv
   float scale_log2;
 };
 

@@ -120,7 +120,8 @@ int swa_prefill_chunk(const void* q, const void* k, const void* v, void* out,
  * k_new,v_new [B, Hkv, D]     bf16
  * ring_k,v    [B, Hkv, W, D]  bf16, updated in place
  * pos         [B] int32 (device), out [B, Hq, D] bf16, slot_out [B] int32 or NULL.
- * W in [1, 65536].  Here Hq / Hkv may exceed 16 when it is a multiple of 16.
+ * W in [1, 65536]; B <= 65535, else HSK_ERR_UNSUPPORTED.  Here Hq / Hkv may
+ * exceed 16 when it is a multiple of 16.
  */
 int swa_decode_ring(const void* q, const void* k_new, const void* v_new,
                     void* ring_k, void* ring_v, const int32_t* pos,

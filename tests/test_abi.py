@@ -68,6 +68,7 @@ def test_decode_ring_validation(lib):
     assert f(P, P, P, P, P, P, P, None, 2, 8, 3, 128, 128, 1.0, None) == SHAPE
     assert f(P, P, P, P, P, P, P, None, 2, 8, 2, 32, 128, 1.0, None) == UNSUP
     assert f(P, P, P, P, P, P, P, None, 2, 40, 2, 128, 128, 1.0, None) == UNSUP
+    assert f(P, P, P, P, P, P, P, None, 65536, 8, 2, 128, 128, 1.0, None) == UNSUP
     assert f(P, P, P, MIS, P, P, P, None, 2, 8, 2, 128, 128, 1.0, None) == ALIGN
     assert f(P, P, P, P, P, P + 2, P, None, 2, 8, 2, 128, 128, 1.0, None) == ALIGN
 
