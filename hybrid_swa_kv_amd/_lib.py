@@ -5,7 +5,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhybrid_swa_kv.so")
+# the in-tree build; HYBRID_SWA_KV_LIB names another build of the same sources
+# (e.g. the host-sanitized one the ABI tests also run against)
+LIB_PATH = os.environ.get("HYBRID_SWA_KV_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                              "libhybrid_swa_kv.so")
 ABI_VERSION = 5  # the signatures below; hsk_abi_version() of the loaded library must match
 
 # every symbol declared in include/hybrid_swa_kv.h
