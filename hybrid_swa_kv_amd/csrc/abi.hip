@@ -122,6 +122,8 @@ int swa_prefill(const void* q, const void* k, const void* v, void* out, int B, i
   if ((long long)L > (1ll << 30) || (long long)B * L * Hq > (1ll << 31) - 1) return HSK_ERR_SHAPE;
   // K/V tiles are fetched with 32-bit byte offsets from each sequence's start
   if (dtype == HSK_BF16 && (long long)L * Hkv * D * 2 >= (1ll << 32)) return HSK_ERR_UNSUPPORTED;
+  // the fp32 path runs a 64-lane wave per (sequence, row, head): 64 B L Hq work-items < 2^32
+  if (dtype == HSK_F32 && (long long)B * L * Hq > (1ll << 26)) return HSK_ERR_UNSUPPORTED;
   if (ring_k && ring_w <= 0) return HSK_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return HSK_ERR_ALIGN;
   if (ring_k && (!aligned16(ring_k) || !aligned16(ring_v))) return HSK_ERR_ALIGN;

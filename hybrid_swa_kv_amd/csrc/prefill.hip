@@ -9,7 +9,8 @@
 // feeds O^T += V^T * P^T directly; V^T comes out of LDS with ds_read_b64_tr_b16.
 // Tiles wholly outside a wave's window are skipped; only edge tiles are masked.
 //
-// fp32 path: plain per-(row, head) online softmax in fp32 for small cases.
+// fp32 path: one wave per (row, head), online softmax over 64-key blocks in fp32,
+// for small cases.
 #include "common.hpp"
 #include "flash_tile.hpp"
 #include "kernels.hpp"
@@ -114,45 +115,71 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_chunk_kernel(PrefillArg
   prefill_body<D, true>(a, smem0, smem1);
 }
 
-// fp32: one thread per (b, row, head); exact fp32 arithmetic with expf.
+// fp32: one wave per (b, row, head), exact fp32 arithmetic with expf.  The
+// visible keys are taken 64 at a time: lane j scores key j0 + j (a sequential
+// fp32 dot product over d), the wave forms the block's maximum and sum and
+// rescales the running state, then each lane accumulates P V for its own
+// output dimensions d = lane + 64 i with the block's probabilities read from LDS.
 template <int D>
-__global__ __launch_bounds__(128) void prefill_f32_kernel(PrefillArgs a) {
-  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long total = (long)a.B * a.L * a.Hq;
-  if (idx >= total) return;
+__global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
+  constexpr int ND = D / 64;  // output dimensions per lane
+  __shared__ float sq[D];
+  __shared__ float sp[64];
+  const long idx = blockIdx.x;  // (b * L + row) * Hq + h
   const int h = (int)(idx % a.Hq);
   const long t = idx / a.Hq;
   const int row = (int)(t % a.L);
   const int b = (int)(t / a.L);
-  const int G = a.Hq / a.Hkv;
-  const int g = h / G;
+  const int g = h / (a.Hq / a.Hkv);
+  const int lane = threadIdx.x;
   const float* qf = (const float*)a.q + ((size_t)(b * (size_t)a.L + row) * a.Hq + h) * D;
   const float* kf = (const float*)a.k + ((size_t)b * a.L * a.Hkv + g) * D;
   const float* vf = (const float*)a.v + ((size_t)b * a.L * a.Hkv + g) * D;
   const size_t rs = (size_t)a.Hkv * D;
-  float q[D], acc[D];
 #pragma unroll
-  for (int d = 0; d < D; ++d) { q[d] = qf[d]; acc[d] = 0.f; }
+  for (int i = 0; i < ND; ++i) sq[lane + 64 * i] = qf[lane + 64 * i];
+  __syncthreads();
   const int lo = max(0, row - a.window + 1);
-  float m = kNegInf, l = 0.f;
-  for (int j = lo; j <= row; ++j) {
-    const float* kr = kf + (size_t)j * rs;
-    float s = 0.f;
+  float m = kNegInf, l = 0.f, acc[ND];
 #pragma unroll
-    for (int d = 0; d < D; ++d) s = fmaf(q[d], kr[d], s);
-    s *= a.scale;
-    const float m_new = fmaxf(m, s);
-    const float alpha = expf(m - m_new);
-    const float p = expf(s - m_new);
-    l = l * alpha + p;
-    const float* vr = vf + (size_t)j * rs;
+  for (int i = 0; i < ND; ++i) acc[i] = 0.f;
+  for (int j0 = lo; j0 <= row; j0 += 64) {
+    const int j = j0 + lane;
+    float s = kNegInf;
+    if (j <= row) {
+      const float4* kr = (const float4*)(kf + (size_t)j * rs);
+      float dot = 0.f;
 #pragma unroll
-    for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vr[d], acc[d] * alpha);
+      for (int d4 = 0; d4 < D / 4; ++d4) {
+        const float4 kv = kr[d4];
+        dot = fmaf(sq[4 * d4], kv.x, dot);
+        dot = fmaf(sq[4 * d4 + 1], kv.y, dot);
+        dot = fmaf(sq[4 * d4 + 2], kv.z, dot);
+        dot = fmaf(sq[4 * d4 + 3], kv.w, dot);
+      }
+      s = dot * a.scale;
+    }
+    const float m_new = fmaxf(m, wave_max(s));
+    const float alpha = (m == kNegInf) ? 0.f : expf(m - m_new);
+    const float p = (j <= row) ? expf(s - m_new) : 0.f;
+    l = fmaf(l, alpha, wave_sum(p));
+    sp[lane] = p;
+    __syncthreads();
+    const int n = min(64, row - j0 + 1);
+#pragma unroll
+    for (int i = 0; i < ND; ++i) acc[i] *= alpha;
+    for (int jj = 0; jj < n; ++jj) {
+      const float pj = sp[jj];
+      const float* vr = vf + (size_t)(j0 + jj) * rs + lane;
+#pragma unroll
+      for (int i = 0; i < ND; ++i) acc[i] = fmaf(pj, vr[64 * i], acc[i]);
+    }
     m = m_new;
+    __syncthreads();  // sp is rewritten by the next block
   }
   float* orow = (float*)a.o + ((size_t)(b * (size_t)a.L + row) * a.Hq + h) * D;
 #pragma unroll
-  for (int d = 0; d < D; ++d) orow[d] = acc[d] / l;
+  for (int i = 0; i < ND; ++i) orow[lane + 64 * i] = acc[i] / l;
 }
 
 // ring copy: positions max(0, L-W) .. L-1 -> slot p mod W of [B, Hkv, W, D]
@@ -195,12 +222,11 @@ hipError_t launch_prefill_bf16(const PrefillArgs& in, hipStream_t stream) {
 }
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
-  const long total = (long)a.B * a.L * a.Hq;
-  const int grid = (int)((total + 127) / 128);
+  const long total = (long)a.B * a.L * a.Hq;  // one wave each; < 2^31 (checked at the boundary)
   if (a.D == 128)
-    hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3(grid), dim3(128), 0, stream, a);
+    hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3((unsigned)total), dim3(64), 0, stream, a);
   else
-    hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3(grid), dim3(128), 0, stream, a);
+    hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3((unsigned)total), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

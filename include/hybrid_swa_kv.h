@@ -68,7 +68,8 @@ int hsk_abi_version(void);
  * q   [B, L, Hq,  D]  dtype        (token-major)
  * k,v [B, L, Hkv, D]  dtype
  * out [B, L, Hq,  D]  dtype, written
- * dtype HSK_BF16 (MFMA path) or HSK_F32 (exact-fp32 path, any L, for small cases).
+ * dtype HSK_BF16 (MFMA path) or HSK_F32 (exact-fp32 path for small cases:
+ * B * L * Hq <= 2^26, else HSK_ERR_UNSUPPORTED).
  * scale > 0 (the softmax scale, usually 1/sqrt(D)).
  * ring_k, ring_v: optional (both NULL or both set), [B, Hkv, ring_w, D] dtype.
  *   When set, the K/V of positions max(0, L - ring_w) .. L-1 are also copied to

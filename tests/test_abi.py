@@ -57,6 +57,7 @@ def test_prefill_validation(lib):
     assert f(P, P, P, P, 1, 8, 2, 2, 128, 0, -1.0, 1, None, None, 0, None) == SHAPE
     assert f(P, P, P, P, 1, 8, 2, 2, 128, 0, 1.0, 1, P, P, 0, None) == SHAPE
     assert f(P, MIS, P, P, 1, 8, 2, 2, 128, 0, 1.0, 1, None, None, 0, None) == ALIGN
+    assert f(P, P, P, P, 1, 1 << 20, 128, 8, 64, 0, 1.0, 0, None, None, 0, None) == UNSUP  # fp32: > 2^26 rows x heads
 
 
 def test_decode_ring_validation(lib):

@@ -30,10 +30,12 @@ def test_tiny_window_fp32_config():
     assert max_abs(out_f64(out), ref) <= F32_TOL
 
 
-@pytest.mark.parametrize("L,Hq,Hkv,D,W", [(37, 4, 2, 128, 5), (200, 2, 1, 64, 0), (130, 3, 3, 64, 64)])
-def test_fp32_small(L, Hq, Hkv, D, W):
-    announce("prefill_f32", L=L, Hq=Hq, Hkv=Hkv, D=D, W=W)
-    q, k, v = _case(2, None, L, Hq, Hkv, D, "f32")
+@pytest.mark.parametrize("B,L,Hq,Hkv,D,W", [(None, 37, 4, 2, 128, 5), (None, 200, 2, 1, 64, 0), (None, 130, 3, 3, 64, 64),
+                                             (None, 300, 4, 2, 128, 0), (2, 193, 4, 1, 128, 129)])
+def test_fp32_small(B, L, Hq, Hkv, D, W):
+    # several 64-key blocks per row (full causal at L 300; window 129), GQA, a batch of 2
+    announce("prefill_f32", B=B, L=L, Hq=Hq, Hkv=Hkv, D=D, W=W)
+    q, k, v = _case(2, B, L, Hq, Hkv, D, "f32")
     out = hsk.swa_prefill(torch.from_numpy(q).to(dev()), torch.from_numpy(k).to(dev()),
                           torch.from_numpy(v).to(dev()), W)
     assert max_abs(out_f64(out), oracle.swa_prefill(q, k, v, W)) <= F32_TOL
