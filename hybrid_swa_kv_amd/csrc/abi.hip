@@ -216,6 +216,7 @@ int kv_quant_int8_b32(const void* x, int8_t* codes, float* scales, int B, int Hk
   if (!x || !codes || !scales) return HSK_ERR_NULL;
   if (B <= 0 || Hkv <= 0 || T < 0 || T % 32 != 0) return HSK_ERR_SHAPE;
   if (!head_dim_ok(D)) return HSK_ERR_UNSUPPORTED;
+  if ((long long)B * Hkv * (T / 32) >= (1ll << 31)) return HSK_ERR_UNSUPPORTED;  // blocks index the grid
   if (!aligned16(x) || !aligned16(codes) || !aligned4(scales)) return HSK_ERR_ALIGN;
   if (T == 0) return HSK_OK;
   hsk::QuantArgs a{};
@@ -314,6 +315,9 @@ int kv_block_means_int8(const int8_t* codes, const float* scales, float* means, 
                         void* stream) {
   if (B <= 0 || Hkv <= 0 || T8 < 0 || T8 % 32 != 0) return HSK_ERR_SHAPE;
   if (!head_dim_ok(D)) return HSK_ERR_UNSUPPORTED;
+  // one thread per (sequence, KV head, block, d): the grid counts them in 256s
+  if ((long long)B * Hkv >= (1ll << 31) || (long long)B * Hkv * (T8 / 32) * D >= (1ll << 39))
+    return HSK_ERR_UNSUPPORTED;
   if (T8 == 0) return HSK_OK;
   if (!codes || !scales || !means) return HSK_ERR_NULL;
   if (!aligned4(scales) || !aligned4(means)) return HSK_ERR_ALIGN;

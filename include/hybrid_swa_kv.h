@@ -143,6 +143,8 @@ int swa_decode_ring(const void* q, const void* k_new, const void* v_new,
  * x      [B, Hkv, T, D] bf16          (T % 32 == 0)
  * codes  [B, Hkv, T, D] int8, written
  * scales [B, Hkv, T/32] fp32, written
+ * Limits: B * Hkv * T / 32 < 2^31 blocks, else HSK_ERR_UNSUPPORTED; T == 0 is a
+ * no-op.
  */
 int kv_quant_int8_b32(const void* x, int8_t* codes, float* scales,
                       int B, int Hkv, int T, int D, void* stream);
@@ -215,7 +217,10 @@ int attn_decode_int8kv_noalloc(const void* q,
  *
  * codes  [B, Hkv, T8, D] int8;  scales [B, Hkv, T8/32] fp32
  * means  [B, Hkv, D, T8/32] fp32, written (d-major)
- * Errors: HSK_ERR_SHAPE unless T8 % 32 == 0; T8 == 0 is a no-op.
+ * Errors: HSK_ERR_SHAPE unless B, Hkv > 0 and T8 % 32 == 0; HSK_ERR_UNSUPPORTED
+ * for D other than 64 or 128, or B * Hkv * (T8/32) * D >= 2^39; T8 == 0 is then
+ * a no-op (the pointers may be NULL); else HSK_ERR_NULL for a NULL pointer and
+ * HSK_ERR_ALIGN for scales or means not 4-byte aligned.
  */
 int kv_block_means_int8(const int8_t* codes, const float* scales, float* means,
                         int B, int Hkv, int T8, int D, void* stream);

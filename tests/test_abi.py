@@ -82,6 +82,19 @@ def test_quant_validation(lib):
     assert f(P, P, P, 1, 1, 32, 256, None) == UNSUP
     assert f(P, MIS, P, 1, 1, 32, 128, None) == ALIGN
     assert f(P, P, P, 1, 1, 0, 128, None) == OK          # empty region: nothing to do
+    assert f(P, P, P, 1 << 16, 1 << 10, 1 << 20, 128, None) == UNSUP  # 2^41 blocks
+
+
+def test_block_means_validation(lib):
+    f = lib.kv_block_means_int8
+    #        codes scales means B Hkv T8 D stream
+    assert f(P, P, P, 0, 1, 32, 128, None) == SHAPE
+    assert f(P, P, P, 1, 1, 33, 128, None) == SHAPE
+    assert f(P, P, P, 1, 1, 32, 96, None) == UNSUP
+    assert f(P, P, P, 1 << 16, 1 << 10, 1 << 20, 128, None) == UNSUP
+    assert f(None, None, None, 1, 1, 0, 128, None) == OK     # empty region: nothing to do
+    assert f(None, P, P, 1, 1, 32, 128, None) == NULL
+    assert f(P, P, P + 2, 1, 1, 32, 128, None) == ALIGN
 
 
 def test_int8_decode_validation(lib):
