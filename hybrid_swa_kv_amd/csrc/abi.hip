@@ -57,7 +57,11 @@ SparsePlan sparse_plan(int B, int Hq, int Hkv, int D, int T8, int Th, int topk) 
   const size_t units = (size_t)B * Hkv;
   p.nblk = T8 / 32;
   p.lmax = topk > 0 ? std::min(p.nblk, G * topk) : 0;
-  p.epsplit = 32;
+  // kept blocks per INT8 split: 64 measured 3 % faster than 32 at batch 16 and
+  // 1984 blocks (fewer records to merge); 128 and 256 were slower (fewer
+  // workgroups than the GPU holds).  At most 256: a wave reads its entries
+  // (every fourth) one per lane.
+  p.epsplit = 64;
   p.nss = (p.lmax + p.epsplit - 1) / p.epsplit;
   p.hsplit = 512;
   p.nsh = (Th + p.hsplit - 1) / p.hsplit;
