@@ -61,3 +61,28 @@ def test_select_brute_force_and_ties():
             assert list(sel[b, h]) == sorted(order[:6])
             assert np.allclose(sc, scores[b, h], rtol=1e-12, atol=0)
     assert scores[0, 0, 5] == scores[0, 0, 2]
+
+
+def test_partial_selection_equals_attention_over_the_gathered_tokens():
+    """A kept block j stands for tokens 32 j .. 32 j + 31: attending the hot tail
+    plus the kept blocks equals torch's attention (fp64, CPU) over exactly those
+    tokens, gathered in order, with no mask (the query sees every cached token)."""
+    import torch
+    import torch.nn.functional as F
+
+    q, kc, ks, vc, vs, kh, vh = _pool(8, 1, 4, 2, 16, 320, 7)
+    kd = oracle.dequant_int8_b32(kc, ks)
+    vd = oracle.dequant_int8_b32(vc, vs)
+    sel = np.array([[[0, 3, 9, -1], [2, -1, -1, -1], [-1, -1, -1, -1], [1, 2, 3, 4]]], dtype=np.int32)
+    got = oracle.attn_decode_int8kv_sparse(q, kc, ks, vc, vs, kh, vh, sel)
+    for h in range(4):
+        g = h // 2
+        blocks = [int(j) for j in sel[0, h] if j >= 0]
+        toks = [t for j in blocks for t in range(32 * j, 32 * j + 32)]
+        kk = np.concatenate([kd[0, g][toks], kh[0, g]], axis=0)
+        vv = np.concatenate([vd[0, g][toks], vh[0, g]], axis=0)
+        want = F.scaled_dot_product_attention(torch.from_numpy(q[0, h][None, None]), torch.from_numpy(kk[None]),
+                                              torch.from_numpy(vv[None]), scale=0.25)[0, 0].numpy()
+        assert np.allclose(got[0, h], want, rtol=0, atol=1e-13), h
+    # the selection changes the result: a head keeping nothing differs from one keeping blocks
+    assert not np.allclose(got[0, 2], got[0, 3])
