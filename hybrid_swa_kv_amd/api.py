@@ -27,28 +27,40 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+def _call(dev, name, *args):
+    """Calls the library entry point `name` with `dev` as the current device (the
+    kernels run there, on a stream of that device)."""
+    with torch.cuda.device(dev):
+        _check(getattr(_lib.load(), name)(*args))
+
+
+def _stream(stream, dev):
+    """torch's current stream of `dev`, or the caller's stream, which must belong to `dev`."""
+    if stream is None:
+        return torch.cuda.current_stream(dev).cuda_stream
+    if stream.device != dev:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {dev}")
+    return stream.cuda_stream
 
 
 def _out(t, name, dtype, shape, device):
     """A caller-supplied output must be exactly what the kernel writes (a contiguous
-    GPU tensor of this dtype and shape); None allocates one."""
+    tensor of this dtype and shape on the inputs' GPU); None allocates one."""
     shape = tuple(int(x) for x in shape)
     if t is None:
         return torch.empty(shape, dtype=dtype, device=device)
     _need(t, name, dtype, shape=shape)
-    _on_gpu(t, name)
+    _same_device(device, t, name)
     return t
 
 
 def _scratch(t, name, nbytes, device):
-    """Workspace: a contiguous GPU tensor of at least nbytes (None allocates one)."""
+    """Workspace: a contiguous tensor of at least nbytes on the inputs' GPU (None
+    allocates one)."""
     if t is None:
         return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
     _need(t, name)
-    _on_gpu(t, name)
+    _same_device(device, t, name)
     return t
 
 
@@ -58,7 +70,7 @@ def _need(t, name, dtype=None, ndim=None, shape=None):
     Every tensor the kernels read or write is checked against the sizes the call
     derives, so a short or mis-shaped buffer is refused here instead of being read
     or written past its end on the device.  The device is checked separately
-    (``_on_gpu``), after all shapes, so shape errors read the same on any device.
+    (``_device``), after all shapes, so shape errors read the same on any device.
     """
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -72,11 +84,28 @@ def _need(t, name, dtype=None, ndim=None, shape=None):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _on_gpu(*named):
-    """named: tensor, name, tensor, name, ... (None tensors are skipped)."""
+def _device(*named):
+    """named: tensor, name, tensor, name, ... (None tensors are skipped).  Every
+    tensor must be on a GPU, and all on the same one (a pointer from another
+    device would be read by kernels that cannot reach it); returns that device."""
+    dev = None
     for t, name in zip(named[::2], named[1::2]):
-        if t is not None and not t.is_cuda:
+        if t is None:
+            continue
+        if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+    return dev
+
+
+def _same_device(dev, t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
 
 
 def _blocks32(T, name):
@@ -112,12 +141,12 @@ def swa_prefill(q, k, v, window: int, scale: float | None = None, out=None, ring
         W = ring_k.shape[2]
         _need(ring_k, "ring_k", dtype, shape=(B, Hkv, W, D))
         _need(ring_v, "ring_v", dtype, shape=(B, Hkv, W, D))
-    _on_gpu(q, "q", k, "k", v, "v", ring_k, "ring_k", ring_v, "ring_v")
-    out = _out(out, "out", q.dtype, q.shape, q.device)
+    dev = _device(q, "q", k, "k", v, "v", ring_k, "ring_k", ring_v, "ring_v")
+    out = _out(out, "out", q.dtype, q.shape, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(_lib.load().swa_prefill(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, L, Hq, Hkv, D, int(window), scale,
-        BF16 if dtype == torch.bfloat16 else F32, _ptr(ring_k), _ptr(ring_v), W, _stream(stream)))
+    _call(dev, "swa_prefill",
+          _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, L, Hq, Hkv, D, int(window), scale,
+          BF16 if dtype == torch.bfloat16 else F32, _ptr(ring_k), _ptr(ring_v), W, _stream(stream, dev))
     return out
 
 
@@ -137,13 +166,13 @@ def swa_decode_ring(q, k_new, v_new, ring_k, ring_v, pos, scale: float | None = 
     _need(k_new, "k_new", torch.bfloat16, shape=(B, Hkv, D))
     _need(v_new, "v_new", torch.bfloat16, shape=(B, Hkv, D))
     _need(pos, "pos", torch.int32, shape=(B,))
-    _on_gpu(q, "q", k_new, "k_new", v_new, "v_new", ring_k, "ring_k", ring_v, "ring_v", pos, "pos")
-    out = _out(out, "out", q.dtype, q.shape, q.device)
-    slot_out = _out(slot_out, "slot_out", torch.int32, (B,), q.device)
+    dev = _device(q, "q", k_new, "k_new", v_new, "v_new", ring_k, "ring_k", ring_v, "ring_v", pos, "pos")
+    out = _out(out, "out", q.dtype, q.shape, dev)
+    slot_out = _out(slot_out, "slot_out", torch.int32, (B,), dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(_lib.load().swa_decode_ring(
-        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(ring_k), _ptr(ring_v), _ptr(pos), _ptr(out), _ptr(slot_out),
-        B, Hq, Hkv, D, W, scale, _stream(stream)))
+    _call(dev, "swa_decode_ring",
+          _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(ring_k), _ptr(ring_v), _ptr(pos), _ptr(out), _ptr(slot_out),
+          B, Hq, Hkv, D, W, scale, _stream(stream, dev))
     return out, slot_out
 
 
@@ -155,10 +184,10 @@ def kv_quant_int8_b32(x, codes=None, scales=None, stream=None):
     _need(x, "x", torch.bfloat16, 4)
     B, Hkv, T, D = x.shape
     nblk = _blocks32(T, "x")
-    _on_gpu(x, "x")
-    codes = _out(codes, "codes", torch.int8, x.shape, x.device)
-    scales = _out(scales, "scales", torch.float32, (B, Hkv, nblk), x.device)
-    _check(_lib.load().kv_quant_int8_b32(_ptr(x), _ptr(codes), _ptr(scales), B, Hkv, T, D, _stream(stream)))
+    dev = _device(x, "x")
+    codes = _out(codes, "codes", torch.int8, x.shape, dev)
+    scales = _out(scales, "scales", torch.float32, (B, Hkv, nblk), dev)
+    _call(dev, "kv_quant_int8_b32", _ptr(x), _ptr(codes), _ptr(scales), B, Hkv, T, D, _stream(stream, dev))
     return codes, scales
 
 
@@ -167,7 +196,8 @@ def attn_decode_int8kv_workspace_size(B, Hq, Hkv, D, T8, Th) -> int:
 
 
 def _int8_pool(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot, k_means=None, with_means=False):
-    """Checks the INT8 + bf16 pool arguments of the decodes; returns (B, Hq, Hkv, D, T8, Th)."""
+    """Checks the INT8 + bf16 pool arguments of the decodes; returns
+    (B, Hq, Hkv, D, T8, Th, device)."""
     _need(q, "q", torch.bfloat16, 3)
     _need(k_hot, "k_hot", torch.bfloat16, 4)
     B, Hq, D = q.shape
@@ -185,10 +215,12 @@ def _int8_pool(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot, k_means=No
         _need(v_scales, "v_scales", torch.float32, shape=(B, Hkv, nblk))
         if with_means:
             _need(k_means, "k_means", torch.float32, shape=(B, Hkv, D, nblk))
-        _on_gpu(k_codes, "k_codes", v_codes, "v_codes", k_scales, "k_scales", v_scales, "v_scales",
-                k_means if with_means else None, "k_means")
-    _on_gpu(q, "q", k_hot, "k_hot", v_hot, "v_hot")
-    return B, Hq, Hkv, D, T8, Th
+    cold = T8 > 0
+    dev = _device(q, "q", k_hot, "k_hot", v_hot, "v_hot",
+                  k_codes if cold else None, "k_codes", v_codes if cold else None, "v_codes",
+                  k_scales if cold else None, "k_scales", v_scales if cold else None, "v_scales",
+                  k_means if cold and with_means else None, "k_means")
+    return B, Hq, Hkv, D, T8, Th, dev
 
 
 def attn_decode_int8kv(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot, scale: float | None = None,
@@ -198,16 +230,16 @@ def attn_decode_int8kv(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot, sc
     q [B, Hq, D] bf16; *_codes [B, Hkv, T8, D] int8; *_scales [B, Hkv, T8/32] fp32;
     *_hot [B, Hkv, Th, D] bf16.  Returns out [B, Hq, D] bf16.
     """
-    B, Hq, Hkv, D, T8, Th = _int8_pool(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot)
-    out = _out(out, "out", torch.bfloat16, q.shape, q.device)
+    B, Hq, Hkv, D, T8, Th, dev = _int8_pool(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot)
+    out = _out(out, "out", torch.bfloat16, q.shape, dev)
     need = attn_decode_int8kv_workspace_size(B, Hq, Hkv, D, T8, Th)
-    workspace = _scratch(workspace, "workspace", need, q.device)
+    workspace = _scratch(workspace, "workspace", need, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(_lib.load().attn_decode_int8kv(
-        _ptr(q), _ptr(k_codes) if T8 else None, _ptr(k_scales) if T8 else None,
-        _ptr(v_codes) if T8 else None, _ptr(v_scales) if T8 else None, _ptr(k_hot), _ptr(v_hot),
-        _ptr(out), B, Hq, Hkv, D, T8, Th, scale, _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
+    _call(dev, "attn_decode_int8kv",
+          _ptr(q), _ptr(k_codes) if T8 else None, _ptr(k_scales) if T8 else None,
+          _ptr(v_codes) if T8 else None, _ptr(v_scales) if T8 else None, _ptr(k_hot), _ptr(v_hot),
+          _ptr(out), B, Hq, Hkv, D, T8, Th, scale, _ptr(workspace), workspace.numel() * workspace.element_size(),
+          _stream(stream, dev))
     return out
 
 
@@ -216,13 +248,13 @@ def attn_decode_int8kv_noalloc(q, k_codes, k_scales, v_codes, v_scales, k_hot, v
     """attn_decode_int8kv with the split records in the library's static device
     array (no workspace argument; nothing allocated when ``out`` is given).
     Calls that overlap on one GPU race on that array."""
-    B, Hq, Hkv, D, T8, Th = _int8_pool(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot)
-    out = _out(out, "out", torch.bfloat16, q.shape, q.device)
+    B, Hq, Hkv, D, T8, Th, dev = _int8_pool(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot)
+    out = _out(out, "out", torch.bfloat16, q.shape, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(_lib.load().attn_decode_int8kv_noalloc(
-        _ptr(q), _ptr(k_codes) if T8 else None, _ptr(k_scales) if T8 else None,
-        _ptr(v_codes) if T8 else None, _ptr(v_scales) if T8 else None, _ptr(k_hot), _ptr(v_hot),
-        _ptr(out), B, Hq, Hkv, D, T8, Th, scale, _stream(stream)))
+    _call(dev, "attn_decode_int8kv_noalloc",
+          _ptr(q), _ptr(k_codes) if T8 else None, _ptr(k_scales) if T8 else None,
+          _ptr(v_codes) if T8 else None, _ptr(v_scales) if T8 else None, _ptr(k_hot), _ptr(v_hot),
+          _ptr(out), B, Hq, Hkv, D, T8, Th, scale, _stream(stream, dev))
     return out
 
 
@@ -245,15 +277,15 @@ def blocksparse_select_attend(q, k, v, block: int = 64, topk: int = 64, window: 
     _need(v, "v", torch.bfloat16, shape=(L, Hkv, D))
     if block <= 0 or L % block != 0:
         raise ValueError(f"L = {L} must be a multiple of block = {block}")
-    _on_gpu(q, "q", k, "k", v, "v")
-    out = _out(out, "out", torch.bfloat16, q.shape, q.device)
-    sel = _out(sel, "sel", torch.int32, (Hq, L // block, topk), q.device)
+    dev = _device(q, "q", k, "k", v, "v")
+    out = _out(out, "out", torch.bfloat16, q.shape, dev)
+    sel = _out(sel, "sel", torch.int32, (Hq, L // block, topk), dev)
     need = blocksparse_workspace_size(L, Hq, Hkv, D, block, topk)
-    workspace = _scratch(workspace, "workspace", need, q.device)
+    workspace = _scratch(workspace, "workspace", need, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(_lib.load().blocksparse_select_attend(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(sel) if topk > 0 else None, L, Hq, Hkv, D, block, topk,
-        window, scale, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    _call(dev, "blocksparse_select_attend",
+          _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(sel) if topk > 0 else None, L, Hq, Hkv, D, block, topk,
+          window, scale, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, dev))
     return out, sel
 
 
@@ -266,9 +298,9 @@ def swa_window_safe_len(slot_pos, match_len, out=None, stream=None):
     _need(slot_pos, "slot_pos", torch.int32, 2)
     B, W = slot_pos.shape
     _need(match_len, "match_len", torch.int32, shape=(B,))
-    _on_gpu(slot_pos, "slot_pos", match_len, "match_len")
-    out = _out(out, "out", torch.int32, (B,), slot_pos.device)
-    _check(_lib.load().swa_window_safe_len(_ptr(slot_pos), _ptr(match_len), _ptr(out), B, W, _stream(stream)))
+    dev = _device(slot_pos, "slot_pos", match_len, "match_len")
+    out = _out(out, "out", torch.int32, (B,), dev)
+    _call(dev, "swa_window_safe_len", _ptr(slot_pos), _ptr(match_len), _ptr(out), B, W, _stream(stream, dev))
     return out
 
 
@@ -287,11 +319,11 @@ def swa_prefill_chunk(q, k, v, ring_k, ring_v, pos0: int, scale: float | None = 
     _need(v, "v", torch.bfloat16, shape=(B, C, Hkv, D))
     _need(ring_k, "ring_k", torch.bfloat16, shape=(B, Hkv, W, D))
     _need(ring_v, "ring_v", torch.bfloat16, shape=(B, Hkv, W, D))
-    _on_gpu(q, "q", k, "k", v, "v", ring_k, "ring_k", ring_v, "ring_v")
-    out = _out(out, "out", q.dtype, q.shape, q.device)
+    dev = _device(q, "q", k, "k", v, "v", ring_k, "ring_k", ring_v, "ring_v")
+    out = _out(out, "out", q.dtype, q.shape, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(_lib.load().swa_prefill_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ring_k), _ptr(ring_v),
-                                         B, C, Hq, Hkv, D, W, int(pos0), scale, _stream(stream)))
+    _call(dev, "swa_prefill_chunk", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ring_k), _ptr(ring_v),
+          B, C, Hq, Hkv, D, W, int(pos0), scale, _stream(stream, dev))
     return out
 
 
@@ -304,10 +336,9 @@ def kv_block_means_int8(codes, scales, means=None, stream=None):
     B, Hkv, T8, D = codes.shape
     nblk = _blocks32(T8, "codes")
     _need(scales, "scales", torch.float32, shape=(B, Hkv, nblk))
-    _on_gpu(codes, "codes", scales, "scales")
-    means = _out(means, "means", torch.float32, (B, Hkv, D, nblk), codes.device)
-    _check(_lib.load().kv_block_means_int8(_ptr(codes), _ptr(scales), _ptr(means), B, Hkv, T8, D,
-                                           _stream(stream)))
+    dev = _device(codes, "codes", scales, "scales")
+    means = _out(means, "means", torch.float32, (B, Hkv, D, nblk), dev)
+    _call(dev, "kv_block_means_int8", _ptr(codes), _ptr(scales), _ptr(means), B, Hkv, T8, D, _stream(stream, dev))
     return means
 
 
@@ -321,16 +352,16 @@ def attn_decode_int8kv_sparse(q, k_codes, k_scales, v_codes, v_scales, k_means, 
 
     Returns (out [B, Hq, D] bf16, sel [B, Hq, topk] int32).
     """
-    B, Hq, Hkv, D, T8, Th = _int8_pool(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot, k_means,
-                                       with_means=True)
-    out = _out(out, "out", torch.bfloat16, q.shape, q.device)
-    sel = _out(sel, "sel", torch.int32, (B, Hq, topk), q.device)
+    B, Hq, Hkv, D, T8, Th, dev = _int8_pool(q, k_codes, k_scales, v_codes, v_scales, k_hot, v_hot, k_means,
+                                            with_means=True)
+    out = _out(out, "out", torch.bfloat16, q.shape, dev)
+    sel = _out(sel, "sel", torch.int32, (B, Hq, topk), dev)
     need = attn_decode_int8kv_sparse_workspace_size(B, Hq, Hkv, D, T8, Th, topk)
-    workspace = _scratch(workspace, "workspace", need, q.device)
+    workspace = _scratch(workspace, "workspace", need, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     opt = (lambda t: _ptr(t) if T8 else None)
-    _check(_lib.load().attn_decode_int8kv_sparse(
-        _ptr(q), opt(k_codes), opt(k_scales), opt(v_codes), opt(v_scales), opt(k_means), _ptr(k_hot), _ptr(v_hot),
-        _ptr(out), _ptr(sel) if topk > 0 else None, B, Hq, Hkv, D, T8, Th, topk, scale, _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+    _call(dev, "attn_decode_int8kv_sparse",
+          _ptr(q), opt(k_codes), opt(k_scales), opt(v_codes), opt(v_scales), opt(k_means), _ptr(k_hot), _ptr(v_hot),
+          _ptr(out), _ptr(sel) if topk > 0 else None, B, Hq, Hkv, D, T8, Th, topk, scale, _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream(stream, dev))
     return out, sel

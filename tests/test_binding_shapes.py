@@ -120,3 +120,24 @@ def test_chunk_and_means_and_prefix_shapes():
     expect(lambda: hsk.kv_block_means_int8(codes, z(2, 2, 3, dtype=f32)), "scales")
     reaches_device_check(lambda: hsk.swa_window_safe_len(z(3, 8, dtype=i32), z(3, dtype=i32)))
     expect(lambda: hsk.swa_window_safe_len(z(3, 8, dtype=i32), z(2, dtype=i32)), "match_len")
+
+
+def test_tensors_and_stream_must_share_one_gpu():
+    """Pointers from two GPUs in one call would be read by kernels on one of them:
+    the binding refuses mixed devices, and a stream of another device."""
+    from types import SimpleNamespace
+
+    from hybrid_swa_kv_amd import api
+
+    def on(dev):
+        return SimpleNamespace(is_cuda=True, device=torch.device(dev))
+
+    assert api._device(None, "a", on("cuda:0"), "b", on("cuda:0"), "c") == torch.device("cuda:0")
+    with pytest.raises(ValueError, match="c is on cuda:1"):
+        api._device(on("cuda:0"), "a", None, "b", on("cuda:1"), "c")
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        api._device(on("cuda:0"), "a", SimpleNamespace(is_cuda=False, device=torch.device("cpu")), "b")
+    with pytest.raises(ValueError, match="out is on cuda:1"):
+        api._same_device(torch.device("cuda:0"), on("cuda:1"), "out")
+    with pytest.raises(ValueError, match="stream is on cuda:1"):
+        api._stream(SimpleNamespace(device=torch.device("cuda:1"), cuda_stream=0), torch.device("cuda:0"))
