@@ -10,7 +10,9 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ * - Every tensor pointer is a DEVICE pointer owned by the caller, all on the
+ *   current HIP device (hipSetDevice), to which `stream` must belong too: the
+ *   kernels are launched there.  The library
  *   never allocates, frees or keeps device memory between calls, holds no global
  *   state, and is reentrant -- except attn_decode_int8kv_noalloc, which uses a
  *   static device array of its own (see there).  Work is enqueued on `stream` (a hipStream_t passed
