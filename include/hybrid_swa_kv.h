@@ -118,6 +118,8 @@ int swa_prefill_chunk(const void* q, const void* k, const void* v, void* out,
  *      the W most recent tokens including the new one; slot s holds position
  *      p - ((p - s) mod W), and slots whose position would be negative are not
  *      attended.  The new token's K/V is taken from k_new/v_new.
+ * A sequence with pos[b] < 0 has no token to decode and is skipped: its ring
+ * rows and slot_out[b] keep their contents and out[b] is all zero.
  *
  * q           [B, Hq,  D]     bf16
  * k_new,v_new [B, Hkv, D]     bf16

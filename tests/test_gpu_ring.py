@@ -89,3 +89,42 @@ def test_ring_window_limit():
     exactly and one that has wrapped."""
     announce("ring_W65536")
     run_case(43, 3, 4, 1, 64, 65536, [0, 65535, 70000])
+
+
+def test_negative_position_skips_the_sequence():
+    """A sequence whose pos is negative (nothing to decode) is skipped: its ring
+    and its slot_out entry keep their bytes and its output rows are zero, while
+    the other sequences of the batch are decoded as usual."""
+    B, Hq, Hkv, D, W = 4, 8, 2, 128, 128
+    pos = np.array([5, -1, 300, -7], dtype=np.int64)
+    announce("ring_negative_pos", B=B, W=W, pos=list(pos))
+    q = synth.normal(711, synth.Q, (B, Hq, D), 1)
+    kn = synth.normal(711, synth.K_NEW, (B, Hkv, D), 1)
+    vn = synth.normal(711, synth.V_NEW, (B, Hkv, D), 1)
+    rk_bits = synth.head_major(711, synth.K, B, Hkv, W, D)
+    rv_bits = synth.head_major(711, synth.V, B, Hkv, W, D)
+    d_rk, d_rv = gpu_bf16(rk_bits), gpu_bf16(rv_bits)
+    slot_out = torch.full((B,), -99, dtype=torch.int32, device="cuda")
+    d_pos = torch.from_numpy(pos.astype(np.int32)).cuda()
+    out, slots = hsk.swa_decode_ring(gpu_bf16(q), gpu_bf16(kn), gpu_bf16(vn), d_rk, d_rv, d_pos, slot_out=slot_out)
+    got_out, got_rk, got_rv = out_f64(out), out_f64(d_rk), out_f64(d_rv)
+    got_slots = slots.cpu().numpy()
+    rk0, rv0 = f64(rk_bits), f64(rv_bits)
+    for b in (1, 3):
+        assert np.all(got_out[b] == 0.0)
+        assert np.array_equal(got_rk[b], rk0[b]) and np.array_equal(got_rv[b], rv0[b])
+        assert got_slots[b] == -99
+    for b in (0, 2):
+        p = int(pos[b])
+        exp_rk = oracle.ring_append(rk0[b:b + 1], [p], f64(kn)[b:b + 1])
+        exp_rv = oracle.ring_append(rv0[b:b + 1], [p], f64(vn)[b:b + 1])
+        assert got_slots[b] == int(oracle.ring_slot(p, W))
+        assert np.array_equal(got_rk[b:b + 1], exp_rk) and np.array_equal(got_rv[b:b + 1], exp_rv)
+        # the logical sequence the ring now holds: positions max(0, p-W+1) .. p
+        first = max(0, p - W + 1)
+        slots_seq = [int(oracle.ring_slot(t, W)) for t in range(first, p + 1)]
+        kseq = exp_rk[:, :, slots_seq]
+        vseq = exp_rv[:, :, slots_seq]
+        ref = oracle.swa_decode(f64(q)[b:b + 1], kseq, vseq, [first], [p], W)
+        ex = bf16_excess(got_out[b:b + 1], ref)
+        assert ex <= 0, (b, ex, max_abs(got_out[b:b + 1], ref))
